@@ -1,0 +1,10 @@
+"""Float64 CPU oracle - TEST INFRASTRUCTURE ONLY.
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg,
+never by the library.  It shares no code with the GPU kernels; see
+oracle.kvzip for the definitions it follows and oracle.brute for the scalar
+brute force that pins it.
+"""
+from .kvzip import (attention_rows, bf16_to_f64, compact, head_scores,
+                    head_scores_parallel, keep_count, row_lse, select,
+                    topk_ascending, visible_keys, workload_head_inputs)

@@ -1,0 +1,9 @@
+"""Seeded synthetic inputs shared by the oracle tests and the GPU path.
+
+Holds workload shapes and the random recipe only; no part of the scoring,
+selection or compaction arithmetic lives here.
+"""
+from .configs import (ALL, BY_NAME, GEMMA12B_16K, LLAMA8B_128K, LLAMA8B_8K,
+                      QWEN14B_32K, TINY, Workload)
+from .generate import (bf16_bits_to_f32, default_workers, f64_to_bf16_bits,
+                       generate_head, generate_workload)
