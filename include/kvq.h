@@ -1,0 +1,144 @@
+/*
+ * kvq.h - query-agnostic KV cache scoring, selection and compaction on AMD
+ * Instinct MI355X (gfx950).  C ABI; every entry point takes plain pointers and
+ * sizes and enqueues work on the caller's HIP stream.
+ *
+ * The computation is the KVzip importance score (page "KVzip: Query-Agnostic
+ * KV Cache Compression with Context Reconstruction"):
+ *   section 2.1  - a prefilled context of n_c tokens caches L x H x n_c KV
+ *                  pairs (KV_c) in a model with L layers and H KV heads, each
+ *                  KV head serving a group of G query heads; the goal is a
+ *                  subset KV_p of KV_c;
+ *   section 3.2  - a teacher-forced pass over the repeat prompt (n_prompt
+ *                  tokens) followed by the context gives, per (l, h), grouped
+ *                  queries Q (G x n_in x d, n_in = n_prompt + n_c) and keys
+ *                  K = [cached keys; new keys] ((n_c + n_in) x d);
+ *                  A = Softmax(Q K^T); the score of cached key j is the max of
+ *                  A[g, i, j] over all g and all n_in rows i;
+ *   section 4.1  - keep the r% highest-scoring pairs.
+ *
+ * Readings fixed by this library where the page is silent:
+ *   - logits are scale * <q, k> with `scale` supplied by the caller
+ *     (normally float32(1 / sqrt(d)));
+ *   - row i (0-based) of the pass sees all n_c cached keys and new keys
+ *     0..i, its own included; every one of the n_in rows counts;
+ *   - the softmax is normalised over every key a row sees, then sliced;
+ *   - the kept count is k = clamp(floor(r * n), 1, n) (the floor rule of the
+ *     SelKV page, "Selective KV cache merging", section 3.1); equal scores
+ *     are broken toward the lower index; kept indices come out ascending.
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   q       bf16  [L][H][G][n_in][d]   query head h*G + g serves KV head h
+ *   k_ctx   bf16  [L][H][n_c][d]       cached keys (KV_c)
+ *   k_new   bf16  [L][H][n_in][d]      keys of the repeat pass
+ *   v_ctx   bf16  [L][H][n_c][d]       cached values
+ *   lse     fp32  [L][H][G][n_in]      natural-log row normaliser
+ *   scores  fp32  [L][H][n_c]          score of every cached key, in [0, 1]
+ *   offsets int64 [L*H + 1]            CSR offsets of the kept sets
+ *   idx     int32 [total]              kept positions j in [0, n_c)
+ *   k_out, v_out bf16 [total][d]       kept rows, grouped by (l, h)
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are owned by the caller; the library never allocates,
+ *     frees or retains them.  bf16 tensors must be 16-byte aligned, fp32 and
+ *     int32 ones 4-byte aligned, int64 ones 8-byte aligned.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error nothing is written and a negative status is returned.
+ *   - Work is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  A launch failure returns KV_ERR_HIP and records the HIP error
+ *     for kv_last_hip_error(); faults during execution surface at the
+ *     caller's next synchronisation.
+ *   - Inputs must be finite.  Calls are reentrant; calls that write the same
+ *     buffers must not overlap.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define KV_OK                0
+#define KV_ERR_INVALID_ARG  -1  /* null pointer, non-positive size, ratio out of (0,1], size overflow */
+#define KV_ERR_UNSUPPORTED  -2  /* d not in {64, 128, 256}, G not in [1, 8], mode not in {0, 1} */
+#define KV_ERR_ALIGNMENT    -3  /* a pointer breaks the alignment rule above */
+#define KV_ERR_CAPACITY     -4  /* idx capacity or workspace too small */
+#define KV_ERR_HIP          -5  /* a HIP runtime call or launch failed */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* kv_status_string(int status);
+
+/* hipError_t of the most recent KV_ERR_HIP on the calling thread (0 if none). */
+int kv_last_hip_error(void);
+
+/* Kept count for a set of n scores at keep ratio r (KVzip section 4.1 budget,
+ * SelKV section 3.1 floor rule): *k_out = clamp(floor(r * n), 1, n), computed
+ * in IEEE double.  Pure host function.  KV_ERR_INVALID_ARG if n < 1, k_out is
+ * NULL or r is not in (0, 1]. */
+int kv_keep_count(int64_t n, double keep_ratio, int64_t* k_out);
+
+/* Pass 1 (KVzip section 3.2, the softmax of A = Softmax(Q K^T)): for every
+ * (l, h, g, i) writes
+ *   lse[l][h][g][i] = ln sum_{j seen by row i} exp(scale * <q_{g,i}, k_j>)
+ * over the n_c cached keys and new keys 0..i.  The attention matrix is never
+ * stored.  Requires L, H >= 1, 1 <= G <= 8, d in {64, 128, 256}, n_c >= 1,
+ * n_prompt >= 0, G * (n_prompt + n_c) < 2^31, scale > 0 and finite. */
+int kvscore_lse(const void* q, const void* k_ctx, const void* k_new, float* lse,
+                int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
+                float scale, void* stream);
+
+/* Pass 2 (KVzip section 3.2, the sliced matrix and its max): for every cached
+ * key writes
+ *   scores[l][h][j] = max_{g, i} exp(scale * <q_{g,i}, k_j> - lse[l][h][g][i])
+ * for j < n_c, i.e. the largest softmax probability key j receives.  lse must
+ * hold pass 1's output for the same inputs.  Every score is written (no
+ * pre-zeroed buffer is needed); the result does not depend on scheduling.
+ * Same requirements as kvscore_lse. */
+int kvscore_colmax(const void* q, const void* k_ctx, const float* lse,
+                   float* scores, int L, int H, int G, int d, int64_t n_c,
+                   int64_t n_prompt, float scale, void* stream);
+
+/* Total kept count for kv_topk_select: L*H*k (mode 0, k = keep count of n_c)
+ * or L*k_L (mode 1, k_L = keep count of H*n_c).  Pure host function. */
+int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
+                  int64_t* total_out);
+
+/* Scratch bytes kv_topk_select needs for these sizes (currently 0 for every
+ * shape; NULL workspace is accepted when the size is 0). */
+size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode);
+
+/* Selection (KVzip section 4.1): keeps the highest scores.
+ *   mode 0: per (l, h), the k = clamp(floor(r * n_c), 1, n_c) largest;
+ *   mode 1: per layer l, the k_L = clamp(floor(r * H * n_c), 1, H * n_c)
+ *           largest of the layer's H * n_c scores (a non-uniform per-head
+ *           budget); heads receive different counts.
+ * Equal scores go to the lower index (j, or h * n_c + j in mode 1).  Writes
+ * offsets[L*H + 1] (offsets[l*H + h] = first kept row of that head) and the
+ * kept positions j into idx, ascending within each head.  scores must be
+ * non-negative (they are ordered by their IEEE bit pattern).  capacity is the
+ * length of idx; KV_ERR_CAPACITY if it is below the total (kv_topk_total). */
+int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
+                   double keep_ratio, int mode, int64_t* offsets, int32_t* idx,
+                   int64_t capacity, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Compaction (KVzip section 2.1, KV_p as a subset of KV_c): for every head
+ * (l, h) and every t in [offsets[l*H+h], offsets[l*H+h+1]) copies
+ *   k_out[t] = k_ctx[l][h][idx[t]],  v_out[t] = v_ctx[l][h][idx[t]]
+ * bit for bit.  total = offsets[L*H] (known on the host from kv_topk_total).
+ * offsets must be non-decreasing with offsets[0] = 0; a row whose index falls
+ * outside [0, n_c) is written as zeros instead of being read.  d in
+ * {64, 128, 256}. */
+int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
+               const int32_t* idx, void* k_out, void* v_out, int L, int H,
+               int d, int64_t n_c, int64_t total, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,11 @@
+"""MI355X-native query-agnostic KV cache scoring and eviction.
+
+KVzip-style maximum cross-attention scoring (pass 1: row lse; pass 2:
+cached-key column max), per-head or per-layer top-k selection and K/V
+compaction, as hand-written gfx950 HIP kernels in libkvq.so behind a C ABI
+(include/kvq.h).  This package is the Python binding of that library; it
+fails loudly when the library has not been built.
+"""
+from .api import (KvqError, evict, kv_compact, kv_keep_count, kv_status_string,
+                  kv_topk_select, kv_topk_total, kv_topk_workspace_bytes,
+                  kvscore_colmax, kvscore_lse, score)

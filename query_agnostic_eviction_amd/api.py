@@ -1,0 +1,206 @@
+"""Python binding of libkvq: the C entry points under the same names, taking
+torch tensors.  Argument marshalling only - every step runs in the HIP
+kernels of libkvq.so; torch supplies device memory and the current stream.
+
+Shapes follow the KVzip page's notation ("KVzip: Query-Agnostic KV Cache
+Compression with Context Reconstruction", sections 2.1 and 3.2):
+    q      bf16 [L, H, G, n_in, d]     k_ctx, v_ctx  bf16 [L, H, n_c, d]
+    k_new  bf16 [L, H, n_in, d]        lse  fp32 [L, H, G, n_in]
+    scores fp32 [L, H, n_c]            offsets int64 [L*H + 1], idx int32
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = _lib.load()
+        name = lib.kv_status_string(status).decode()
+        extra = ""
+        if status == _lib.KV_ERR_HIP:
+            extra = f" (hipError {lib.kv_last_hip_error()})"
+        super().__init__(f"{fn} failed: {name}{extra}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != _lib.KV_OK:
+        raise KvqError(fn, status)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# host helpers
+# ---------------------------------------------------------------------------
+def kv_status_string(status: int) -> str:
+    return _lib.load().kv_status_string(status).decode()
+
+
+def kv_keep_count(n: int, keep_ratio: float) -> int:
+    out = ctypes.c_int64()
+    _check("kv_keep_count", _lib.load().kv_keep_count(n, keep_ratio, ctypes.byref(out)))
+    return out.value
+
+
+def kv_topk_total(L: int, H: int, n_c: int, keep_ratio: float, mode: int) -> int:
+    out = ctypes.c_int64()
+    _check("kv_topk_total",
+           _lib.load().kv_topk_total(L, H, n_c, keep_ratio, mode, ctypes.byref(out)))
+    return out.value
+
+
+def kv_topk_workspace_bytes(L: int, H: int, n_c: int, mode: int) -> int:
+    return int(_lib.load().kv_topk_workspace_bytes(L, H, n_c, mode))
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+def _score_dims(q, k_ctx):
+    if q.dim() != 5 or k_ctx.dim() != 4:
+        raise ValueError("q must be [L,H,G,n_in,d] and k_ctx [L,H,n_c,d]")
+    L, H, G, n_in, d = q.shape
+    n_c = k_ctx.shape[2]
+    if tuple(k_ctx.shape) != (L, H, n_c, d) or n_in < n_c:
+        raise ValueError("q / k_ctx shapes disagree")
+    return L, H, G, d, n_c, n_in - n_c
+
+
+def kvscore_lse(q: torch.Tensor, k_ctx: torch.Tensor, k_new: torch.Tensor,
+                lse: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                stream=None) -> torch.Tensor:
+    """Pass 1: lse[l,h,g,i] over cached keys and causal new keys."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_ctx, torch.bfloat16, "k_ctx")
+    _dev(k_new, torch.bfloat16, "k_new")
+    L, H, G, d, n_c, n_prompt = _score_dims(q, k_ctx)
+    if tuple(k_new.shape) != (L, H, n_c + n_prompt, d):
+        raise ValueError("k_new must be [L,H,n_in,d]")
+    if lse is None:
+        lse = torch.empty((L, H, G, n_c + n_prompt), dtype=torch.float32, device=q.device)
+    _dev(lse, torch.float32, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("kvscore_lse", _lib.load().kvscore_lse(
+        _ptr(q), _ptr(k_ctx), _ptr(k_new), _ptr(lse), L, H, G, d, n_c, n_prompt,
+        float(scale), _stream(stream)))
+    return lse
+
+
+def kvscore_colmax(q: torch.Tensor, k_ctx: torch.Tensor, lse: torch.Tensor,
+                   scores: Optional[torch.Tensor] = None,
+                   scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """Pass 2: scores[l,h,j] = max_{g,i} exp(scale q.k_j - lse)."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_ctx, torch.bfloat16, "k_ctx")
+    _dev(lse, torch.float32, "lse")
+    L, H, G, d, n_c, n_prompt = _score_dims(q, k_ctx)
+    if tuple(lse.shape) != (L, H, G, n_c + n_prompt):
+        raise ValueError("lse must be [L,H,G,n_in]")
+    if scores is None:
+        scores = torch.empty((L, H, n_c), dtype=torch.float32, device=q.device)
+    _dev(scores, torch.float32, "scores")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("kvscore_colmax", _lib.load().kvscore_colmax(
+        _ptr(q), _ptr(k_ctx), _ptr(lse), _ptr(scores), L, H, G, d, n_c, n_prompt,
+        float(scale), _stream(stream)))
+    return scores
+
+
+def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
+                   offsets: Optional[torch.Tensor] = None,
+                   idx: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Kept positions per head (mode 0) or per layer (mode 1), CSR form."""
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 3:
+        raise ValueError("scores must be [L,H,n_c]")
+    L, H, n_c = scores.shape
+    total = kv_topk_total(L, H, n_c, keep_ratio, mode)
+    if offsets is None:
+        offsets = torch.empty(L * H + 1, dtype=torch.int64, device=scores.device)
+    if idx is None:
+        idx = torch.empty(total, dtype=torch.int32, device=scores.device)
+    _dev(offsets, torch.int64, "offsets")
+    _dev(idx, torch.int32, "idx")
+    ws_bytes = kv_topk_workspace_bytes(L, H, n_c, mode)
+    ws = None
+    if ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    _check("kv_topk_select", _lib.load().kv_topk_select(
+        _ptr(scores), L, H, n_c, float(keep_ratio), mode, _ptr(offsets), _ptr(idx),
+        idx.numel(), _ptr(ws), ws_bytes, _stream(stream)))
+    return offsets, idx
+
+
+def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
+               idx: torch.Tensor, k_out: Optional[torch.Tensor] = None,
+               v_out: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gather the kept rows of K and V (bit copies)."""
+    _dev(k_ctx, torch.bfloat16, "k_ctx")
+    _dev(v_ctx, torch.bfloat16, "v_ctx")
+    _dev(offsets, torch.int64, "offsets")
+    _dev(idx, torch.int32, "idx")
+    if k_ctx.dim() != 4 or v_ctx.shape != k_ctx.shape:
+        raise ValueError("k_ctx / v_ctx must both be [L,H,n_c,d]")
+    L, H, n_c, d = k_ctx.shape
+    if offsets.numel() != L * H + 1:
+        raise ValueError("offsets must hold L*H+1 entries")
+    total = idx.numel()
+    if k_out is None:
+        k_out = torch.empty((total, d), dtype=torch.bfloat16, device=k_ctx.device)
+    if v_out is None:
+        v_out = torch.empty((total, d), dtype=torch.bfloat16, device=k_ctx.device)
+    _dev(k_out, torch.bfloat16, "k_out")
+    _dev(v_out, torch.bfloat16, "v_out")
+    if k_out.shape[0] < total or v_out.shape[0] < total:
+        raise ValueError("k_out / v_out too small")
+    _check("kv_compact", _lib.load().kv_compact(
+        _ptr(k_ctx), _ptr(v_ctx), _ptr(offsets), _ptr(idx), _ptr(k_out), _ptr(v_out),
+        L, H, d, n_c, total, _stream(stream)))
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# the whole path
+# ---------------------------------------------------------------------------
+def score(q, k_ctx, k_new, scale=None, stream=None):
+    """(scores, lse) of every cached key: pass 1 then pass 2."""
+    lse = kvscore_lse(q, k_ctx, k_new, scale=scale, stream=stream)
+    scores = kvscore_colmax(q, k_ctx, lse, scale=scale, stream=stream)
+    return scores, lse
+
+
+def evict(q, k_ctx, k_new, v_ctx, keep_ratio, mode=0, scale=None, stream=None):
+    """Score, select and compact: returns (k_out, v_out, offsets, idx, scores)."""
+    scores, _ = score(q, k_ctx, k_new, scale=scale, stream=stream)
+    offsets, idx = kv_topk_select(scores, keep_ratio, mode, stream=stream)
+    k_out, v_out = kv_compact(k_ctx, v_ctx, offsets, idx, stream=stream)
+    return k_out, v_out, offsets, idx, scores

@@ -1,0 +1,102 @@
+// Compaction of the cache to the kept pairs (KVzip page, "KVzip:
+// Query-Agnostic KV Cache Compression with Context Reconstruction", section
+// 2.1: the pruned cache KV_p is a subset of KV_c).
+//
+//   k_out[t] = k_ctx[l][h][idx[t]],  v_out[t] = v_ctx[l][h][idx[t]]
+//   for t in [offsets[l*H+h], offsets[l*H+h+1])
+//
+// A pure HBM-bound gather: each workgroup copies 64 consecutive output rows
+// of K and V with 16-byte vector loads and stores (a row of d bf16 values is
+// d/8 such chunks, contiguous in memory).  One wave first resolves each
+// row's source (head by binary search of the CSR offsets, then its index)
+// into an LDS table, so the copy itself is branch-free.  Every address is
+// bounded by (l*H+h) < L*H and 0 <= idx < n_c, so a malformed index yields a
+// zero row, never a stray read.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kCpRows = 64;  // output rows per workgroup
+
+template <int D>
+__global__ __launch_bounds__(256) void compact_kernel(
+    const uint16_t* __restrict__ k_ctx, const uint16_t* __restrict__ v_ctx,
+    const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
+    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, int LH,
+    int64_t n_c, int64_t total) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 256 / CPR;      // rows per pass of the block
+  constexpr int IT = kCpRows / RPI;
+
+  __shared__ int64_t src_row[kCpRows];  // lh * n_c + idx, or -1 for a zero row
+
+  const int64_t t0 = (int64_t)blockIdx.x * kCpRows;
+  if (threadIdx.x < kCpRows) {
+    const int64_t t = t0 + threadIdx.x;
+    int64_t r = -1;
+    if (t < total) {
+      // head of row t: the largest lh with offsets[lh] <= t
+      int lo = 0, hi = LH - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int64_t j = idx[t];
+      if (j >= 0 && j < n_c) r = (int64_t)lo * n_c + j;
+    }
+    src_row[threadIdx.x] = r;
+  }
+  __syncthreads();
+
+  const int c = threadIdx.x % CPR, rr = threadIdx.x / CPR;
+  u32x4 kv[IT], vv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    // branch-free: read a valid row (row 0 for a rejected index), then mask
+    const int64_t r = src_row[it * RPI + rr];
+    const size_t src = (size_t)(r < 0 ? 0 : r) * D + c * 8;
+    const uint32_t keep = r < 0 ? 0u : 0xffffffffu;
+    kv[it] = ldg16(k_ctx + src) & keep;
+    vv[it] = ldg16(v_ctx + src) & keep;
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t t = t0 + it * RPI + rr;
+    if (t < total) {
+      *reinterpret_cast<u32x4*>(k_out + (size_t)t * D + c * 8) = kv[it];
+      *reinterpret_cast<u32x4*>(v_out + (size_t)t * D + c * 8) = vv[it];
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_compact_d(const uint16_t* k_ctx, const uint16_t* v_ctx,
+                            const int64_t* offsets, const int32_t* idx,
+                            uint16_t* k_out, uint16_t* v_out, int LH,
+                            int64_t n_c, int64_t total, hipStream_t stream) {
+  const int64_t grid = (total + kCpRows - 1) / kCpRows;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_kernel<D>, dim3((unsigned)grid), dim3(256), 0,
+                     stream, k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c,
+                     total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
+                          const int64_t* offsets, const int32_t* idx,
+                          uint16_t* k_out, uint16_t* v_out, int LH, int d,
+                          int64_t n_c, int64_t total, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_compact_d<64>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
+    case 128: return launch_compact_d<128>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
+    case 256: return launch_compact_d<256>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

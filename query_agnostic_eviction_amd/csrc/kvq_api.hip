@@ -1,0 +1,167 @@
+// C ABI of libkvq: argument checks on the host, then one enqueue per call on
+// the caller's stream.  Declarations and contracts live in include/kvq.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KV_OK;
+  g_last_hip = (int)e;
+  return KV_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+bool valid_ratio(double r) { return r > 0.0 && r <= 1.0; }  // false for NaN
+
+int64_t keep_count_of(int64_t n, double r) {
+  double f = floor(r * (double)n);
+  int64_t k = (int64_t)f;
+  if (k < 1) k = 1;
+  if (k > n) k = n;
+  return k;
+}
+
+// Shared checks of the two scoring passes.
+int check_score_args(int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
+                     float scale, kvq::ScoreShape* out) {
+  if (L < 1 || H < 1 || n_c < 1 || n_prompt < 0) return KV_ERR_INVALID_ARG;
+  if (!(scale > 0.0f) || !isfinite(scale)) return KV_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
+  if (G < 1 || G > 8) return KV_ERR_UNSUPPORTED;
+  const int64_t n_in = n_prompt + n_c;
+  if (n_c >= (int64_t)1 << 31 || (int64_t)G * n_in >= (int64_t)1 << 31)
+    return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  out->L = L;
+  out->H = H;
+  out->G = G;
+  out->d = d;
+  out->n_c = (int)n_c;
+  out->n_in = (int)n_in;
+  out->scale = scale;
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_string(int status) {
+  switch (status) {
+    case KV_OK: return "KV_OK";
+    case KV_ERR_INVALID_ARG: return "KV_ERR_INVALID_ARG";
+    case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
+    case KV_ERR_ALIGNMENT: return "KV_ERR_ALIGNMENT";
+    case KV_ERR_CAPACITY: return "KV_ERR_CAPACITY";
+    case KV_ERR_HIP: return "KV_ERR_HIP";
+    default: return "KV_ERR_UNKNOWN";
+  }
+}
+
+int kv_last_hip_error(void) { return g_last_hip; }
+
+int kv_keep_count(int64_t n, double keep_ratio, int64_t* k_out) {
+  if (!k_out || n < 1 || !valid_ratio(keep_ratio)) return KV_ERR_INVALID_ARG;
+  *k_out = keep_count_of(n, keep_ratio);
+  return KV_OK;
+}
+
+int kvscore_lse(const void* q, const void* k_ctx, const void* k_new, float* lse,
+                int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
+                float scale, void* stream) {
+  if (!q || !k_ctx || !k_new || !lse) return KV_ERR_INVALID_ARG;
+  kvq::ScoreShape s;
+  int st = check_score_args(L, H, G, d, n_c, n_prompt, scale, &s);
+  if (st != KV_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_ctx, 16) || !aligned(k_new, 16) || !aligned(lse, 4))
+    return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_lse(static_cast<const uint16_t*>(q),
+                                    static_cast<const uint16_t*>(k_ctx),
+                                    static_cast<const uint16_t*>(k_new), lse, s,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int kvscore_colmax(const void* q, const void* k_ctx, const float* lse,
+                   float* scores, int L, int H, int G, int d, int64_t n_c,
+                   int64_t n_prompt, float scale, void* stream) {
+  if (!q || !k_ctx || !lse || !scores) return KV_ERR_INVALID_ARG;
+  kvq::ScoreShape s;
+  int st = check_score_args(L, H, G, d, n_c, n_prompt, scale, &s);
+  if (st != KV_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_ctx, 16) || !aligned(lse, 4) || !aligned(scores, 4))
+    return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_colmax(static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k_ctx), lse,
+                                       scores, s, static_cast<hipStream_t>(stream)));
+}
+
+int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
+                  int64_t* total_out) {
+  if (!total_out || L < 1 || H < 1 || n_c < 1 || !valid_ratio(keep_ratio))
+    return KV_ERR_INVALID_ARG;
+  if (mode != 0 && mode != 1) return KV_ERR_UNSUPPORTED;
+  if ((int64_t)H * n_c >= (int64_t)1 << 31 || (int64_t)L * H >= (int64_t)1 << 31)
+    return KV_ERR_INVALID_ARG;
+  if (mode == 0)
+    *total_out = (int64_t)L * H * keep_count_of(n_c, keep_ratio);
+  else
+    *total_out = (int64_t)L * keep_count_of((int64_t)H * n_c, keep_ratio);
+  return KV_OK;
+}
+
+size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode) {
+  (void)L; (void)H; (void)n_c; (void)mode;
+  return 0;
+}
+
+int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
+                   double keep_ratio, int mode, int64_t* offsets, int32_t* idx,
+                   int64_t capacity, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  (void)workspace;
+  if (!scores || !offsets || !idx) return KV_ERR_INVALID_ARG;
+  int64_t total = 0;
+  int st = kv_topk_total(L, H, n_c, keep_ratio, mode, &total);
+  if (st != KV_OK) return st;
+  if (!aligned(scores, 4) || !aligned(offsets, 8) || !aligned(idx, 4))
+    return KV_ERR_ALIGNMENT;
+  if (capacity < total || workspace_bytes < kv_topk_workspace_bytes(L, H, n_c, mode))
+    return KV_ERR_CAPACITY;
+  const int64_t k = mode == 0 ? keep_count_of(n_c, keep_ratio)
+                              : keep_count_of((int64_t)H * n_c, keep_ratio);
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_topk(scores, L, H, (int)n_c, mode, k, offsets,
+                                     idx, static_cast<hipStream_t>(stream)));
+}
+
+int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
+               const int32_t* idx, void* k_out, void* v_out, int L, int H,
+               int d, int64_t n_c, int64_t total, void* stream) {
+  if (!k_ctx || !v_ctx || !offsets || !idx || !k_out || !v_out)
+    return KV_ERR_INVALID_ARG;
+  if (L < 1 || H < 1 || n_c < 1 || total < 0) return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  if (total > (int64_t)L * H * n_c) return KV_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
+  if (!aligned(k_ctx, 16) || !aligned(v_ctx, 16) || !aligned(k_out, 16) ||
+      !aligned(v_out, 16) || !aligned(offsets, 8) || !aligned(idx, 4))
+    return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_compact(
+      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx),
+      offsets, idx, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
+      L * H, d, n_c, total, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

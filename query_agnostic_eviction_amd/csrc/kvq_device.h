@@ -1,0 +1,62 @@
+// Device-side helpers shared by the gfx950 kernels of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs each
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D += A * B on the 32x32x16 bf16 matrix core op.  Lane l supplies
+// A[l % 32][8 * (l / 32) + 0..7] and B[8 * (l / 32) + 0..7][l % 32]; it gets
+// back D[8 * (a / 4) + 4 * (l / 32) + a % 4][l % 32] in element a of the
+// accumulator, so each lane holds 16 rows of a single output column.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (within a 32-row block) of accumulator element a held by lane l.
+__device__ __forceinline__ int acc_row(int a, int lane) {
+  return 8 * (a >> 2) + 4 * (lane >> 5) + (a & 3);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero16() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// Workgroups are handed to the 8 dies round-robin (block b runs on die
+// b % 8).  Renumber them so each die receives one contiguous range of logical
+// ids: neighbouring work (the same head) then shares that die's L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  const int xcd = bid % kXcds;
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  return xcd * q + (xcd < r ? xcd : r) + bid / kXcds;
+}
+
+}  // namespace kvq

@@ -1,0 +1,169 @@
+"""C ABI of libkvq on the host (no GPU): exported symbols and argument checks.
+
+Every call here fails validation before any HIP call is made, so nothing is
+launched; fake but well-aligned pointer values stand in for device buffers.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from query_agnostic_eviction_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, INV, UNS, ALN, CAP = 0, -1, -2, -3, -4
+P = ctypes.c_void_p(0x10000)      # aligned fake pointer
+P2 = ctypes.c_void_p(0x10002)     # 2-byte aligned only
+P4 = ctypes.c_void_p(0x10004)     # 4-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv\w*)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    declared = _declared()
+    assert set(declared) == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert hasattr(lib, s)
+
+
+def test_status_strings(lib):
+    names = {0: b"KV_OK", -1: b"KV_ERR_INVALID_ARG", -2: b"KV_ERR_UNSUPPORTED",
+             -3: b"KV_ERR_ALIGNMENT", -4: b"KV_ERR_CAPACITY", -5: b"KV_ERR_HIP"}
+    for k, v in names.items():
+        assert lib.kv_status_string(k) == v
+    assert lib.kv_status_string(42) == b"KV_ERR_UNKNOWN"
+    assert lib.kv_last_hip_error() == 0
+
+
+def test_keep_count_matches_oracle(lib):
+    rng = np.random.default_rng(0)
+    out = ctypes.c_int64()
+    cases = [(512, 0.3), (8192, 0.3), (32768, 0.25), (131072, 0.3), (16384, 0.1),
+             (131072, 0.1), (1, 1.0), (7, 0.999999), (10, 0.05)]
+    cases += [(int(rng.integers(1, 10 ** 7)), float(rng.uniform(1e-6, 1.0))) for _ in range(500)]
+    for n, r in cases:
+        assert lib.kv_keep_count(n, r, ctypes.byref(out)) == OK
+        assert out.value == oracle.keep_count(n, r), (n, r)
+    for bad in (0.0, -1.0, 1.5, math.nan, math.inf):
+        assert lib.kv_keep_count(10, bad, ctypes.byref(out)) == INV
+    assert lib.kv_keep_count(0, 0.5, ctypes.byref(out)) == INV
+    assert lib.kv_keep_count(10, 0.5, None) == INV
+
+
+def test_topk_total(lib):
+    out = ctypes.c_int64()
+    assert lib.kv_topk_total(32, 8, 8192, 0.3, 0, ctypes.byref(out)) == OK
+    assert out.value == 256 * 2457
+    assert lib.kv_topk_total(48, 8, 16384, 0.1, 1, ctypes.byref(out)) == OK
+    assert out.value == 48 * 13107
+    assert lib.kv_topk_total(48, 8, 16384, 0.1, 2, ctypes.byref(out)) == UNS
+    assert lib.kv_topk_total(0, 8, 16384, 0.1, 0, ctypes.byref(out)) == INV
+    assert lib.kv_topk_workspace_bytes(32, 8, 8192, 0) == 0
+
+
+def _lse(lib, q=P, kc=P, kn=P, lse=P, L=1, H=1, G=4, d=128, n_c=16, n_p=2, scale=0.1):
+    return lib.kvscore_lse(q, kc, kn, lse, L, H, G, d, n_c, n_p, scale, NUL)
+
+
+def _col(lib, q=P, kc=P, lse=P, sc=P, L=1, H=1, G=4, d=128, n_c=16, n_p=2, scale=0.1):
+    return lib.kvscore_colmax(q, kc, lse, sc, L, H, G, d, n_c, n_p, scale, NUL)
+
+
+@pytest.mark.parametrize("fn", [_lse, _col])
+def test_score_validation(lib, fn):
+    assert fn(lib, q=NUL) == INV
+    assert fn(lib, kc=NUL) == INV
+    assert fn(lib, L=0) == INV
+    assert fn(lib, H=-1) == INV
+    assert fn(lib, n_c=0) == INV
+    assert fn(lib, n_p=-1) == INV
+    for s in (0.0, -0.5, math.nan, math.inf):
+        assert fn(lib, scale=s) == INV
+    for d in (0, 32, 96, 512):
+        assert fn(lib, d=d) == UNS
+    for g in (0, 9, -1):
+        assert fn(lib, G=g) == UNS
+    assert fn(lib, G=8, n_c=2 ** 28, n_p=0) == INV       # G * n_in >= 2^31
+    assert fn(lib, n_c=2 ** 31, G=1, n_p=0) == INV
+    assert fn(lib, q=P2) == ALN
+    assert fn(lib, kc=P4) == ALN
+
+
+def test_score_validation_specific(lib):
+    assert _lse(lib, kn=NUL) == INV
+    assert _lse(lib, lse=NUL) == INV
+    assert _lse(lib, kn=P4) == ALN
+    assert _lse(lib, lse=P2) == ALN
+    assert _col(lib, lse=NUL) == INV
+    assert _col(lib, sc=NUL) == INV
+    assert _col(lib, sc=P2) == ALN
+
+
+def _sel(lib, sc=P, L=2, H=2, n_c=100, r=0.3, mode=0, off=P, idx=P, cap=1000,
+         ws=NUL, wsb=0):
+    return lib.kv_topk_select(sc, L, H, n_c, r, mode, off, idx, cap, ws, wsb, NUL)
+
+
+def test_select_validation(lib):
+    assert _sel(lib, sc=NUL) == INV
+    assert _sel(lib, off=NUL) == INV
+    assert _sel(lib, idx=NUL) == INV
+    for r in (0.0, 1.01, -0.2, math.nan):
+        assert _sel(lib, r=r) == INV
+    assert _sel(lib, mode=2) == UNS
+    assert _sel(lib, mode=-1) == UNS
+    assert _sel(lib, n_c=0) == INV
+    assert _sel(lib, cap=4 * 30 - 1) == CAP
+    assert _sel(lib, mode=1, cap=2 * 60 - 1) == CAP
+    assert _sel(lib, off=P4) == ALN
+    assert _sel(lib, sc=P2) == ALN
+
+
+def _cmp(lib, kc=P, vc=P, off=P, idx=P, ko=P, vo=P, L=2, H=2, d=128, n_c=100, total=120):
+    return lib.kv_compact(kc, vc, off, idx, ko, vo, L, H, d, n_c, total, NUL)
+
+
+def test_compact_validation(lib):
+    for name in ("kc", "vc", "off", "idx", "ko", "vo"):
+        assert _cmp(lib, **{name: NUL}) == INV
+    assert _cmp(lib, d=32) == UNS
+    assert _cmp(lib, d=100) == UNS
+    assert _cmp(lib, total=-1) == INV
+    assert _cmp(lib, total=401) == INV                # more rows than L*H*n_c
+    assert _cmp(lib, L=0) == INV
+    assert _cmp(lib, ko=P4) == ALN
+    assert _cmp(lib, off=P4) == ALN
+    assert _cmp(lib, idx=P2) == ALN
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    import query_agnostic_eviction_amd as kvq
+    q = torch.zeros((1, 1, 1, 4, 64), dtype=torch.bfloat16)
+    k = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kvq.kvscore_lse(q, k, k)
+    with pytest.raises(ValueError):
+        kvq.kv_topk_select(torch.zeros((1, 1, 4)), 0.5)

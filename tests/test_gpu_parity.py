@@ -1,0 +1,269 @@
+"""GPU parity: libkvq (through its C ABI) against the float64 oracle.
+
+Scores and lse within the tolerances of parity_util; top-k on oracle scores
+and compaction bit-exact; top-k on GPU scores exact outside the near-tie band.
+Definitions: KVzip page ("KVzip: Query-Agnostic KV Cache Compression with
+Context Reconstruction"), section 3.2 (score), section 4.1 (budget).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import query_agnostic_eviction_amd as kvq
+from parity_util import (check_lse, check_scores, check_topk_band, dev_bf16_bits,
+                         head_kept, oracle_head, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+WORKERS = min(16, synth.default_workers())
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    kvq.api._lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _upload(gen):
+    return {k: to_dev_bf16(v) for k, v in gen.items()}
+
+
+def _run(w, dev, mode=0):
+    lse = kvq.kvscore_lse(dev["q"], dev["k_ctx"], dev["k_new"], scale=float(w.scale))
+    sc = kvq.kvscore_colmax(dev["q"], dev["k_ctx"], lse, scale=float(w.scale))
+    off, idx = kvq.kv_topk_select(sc, w.keep_ratio, mode)
+    ko, vo = kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], off, idx)
+    torch.cuda.synchronize()
+    return dict(lse=lse, scores=sc, offsets=off, idx=idx, k_out=ko, v_out=vo)
+
+
+def _full_check(w, gen, out, heads=None, mode=0):
+    """Oracle on every head listed (default: all) of a fully generated input."""
+    L, H = w.L, w.H
+    heads = heads or [(l, h) for l in range(L) for h in range(H)]
+    lse_g = out["lse"].cpu().numpy()
+    sc_g = out["scores"].cpu().numpy()
+    S_ref = np.zeros((L, H, w.n_c))
+    for (l, h) in heads:
+        hg = {k: gen[k][l, h] for k in ("q", "k_ctx", "k_new")}
+        S, lse = oracle_head(hg, float(w.scale), workers=WORKERS if w.n_c > 2000 else 1)
+        check_lse(lse_g[l, h], lse, f"lse[{l},{h}]")
+        check_scores(sc_g[l, h], S, f"scores[{l},{h}]")
+        S_ref[l, h] = S
+    return S_ref
+
+
+def _select_checks(w, gen, out, S_ref, heads, mode):
+    off = out["offsets"].cpu().numpy()
+    idx = out["idx"].cpu().numpy()
+    if mode == 0:
+        k = oracle.keep_count(w.n_c, w.keep_ratio)
+        assert np.array_equal(off, np.arange(w.L * w.H + 1) * k)
+        for (l, h) in heads:
+            check_topk_band(head_kept(off, idx, l * w.H + h), S_ref[l, h], k)
+    # top-k of the oracle's own scores (rounded to fp32) must be bit-exact
+    s32 = torch.from_numpy(S_ref.astype(np.float32)).cuda()
+    o2, i2 = kvq.kv_topk_select(s32, w.keep_ratio, mode)
+    ro, ri = oracle.select(S_ref.astype(np.float32), w.keep_ratio, mode)
+    assert np.array_equal(o2.cpu().numpy(), ro)
+    assert np.array_equal(i2.cpu().numpy(), ri)
+    # compaction of the oracle's kept set must be bit-exact
+    ko, vo = kvq.kv_compact(to_dev_bf16(gen["k_ctx"]), to_dev_bf16(gen["v_ctx"]),
+                            torch.from_numpy(ro).cuda(), torch.from_numpy(ri).cuda())
+    rko, rvo = oracle.compact(gen["k_ctx"], gen["v_ctx"], ro, ri)
+    assert np.array_equal(dev_bf16_bits(ko), rko)
+    assert np.array_equal(dev_bf16_bits(vo), rvo)
+
+
+# ---------------------------------------------------------------------------
+def test_tiny_end_to_end():
+    w = synth.TINY
+    _say("case: tiny", w)
+    gen = synth.generate_workload(w, workers=1)
+    out = _run(w, _upload(gen))
+    S_ref = _full_check(w, gen, out)
+    _select_checks(w, gen, out, S_ref, [(0, 0)], 0)
+    # compacted rows are the kept rows of the input
+    idx = out["idx"].cpu().numpy()
+    assert np.array_equal(dev_bf16_bits(out["k_out"]), gen["k_ctx"][0, 0][idx])
+    assert np.array_equal(dev_bf16_bits(out["v_out"]), gen["v_ctx"][0, 0][idx])
+
+
+RAGGED = [
+    # (base, G, d, n_c, n_prompt, L, H)
+    ("llama3.1-8b-8k", 1, 64, 1, 0, 1, 1),
+    ("llama3.1-8b-8k", 1, 64, 1000, 3, 1, 2),
+    ("gemma3-12b-16k", 2, 256, 300, 32, 2, 1),
+    ("llama3.1-8b-8k", 3, 128, 777, 5, 1, 1),
+    ("qwen2.5-14b-32k", 5, 128, 200, 32, 1, 2),
+    ("llama3.1-8b-8k", 8, 64, 129, 7, 1, 1),
+    ("llama3.1-8b-8k", 4, 128, 64, 0, 1, 1),
+    ("gemma3-12b-16k", 7, 256, 45, 1, 1, 1),
+    ("llama3.1-8b-128k", 4, 128, 4300, 32, 1, 1),
+    ("tiny", 6, 64, 2049, 17, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"G{c[1]}-d{c[2]}-nc{c[3]}-np{c[4]}" for c in RAGGED])
+def test_ragged_shapes(case):
+    base, G, d, n_c, n_p, L, H = case
+    w = synth.BY_NAME[base].shrink(G=G, d=d, n_c=n_c, n_prompt=n_p, L=L, H=H,
+                                   rank=min(synth.BY_NAME[base].rank, d))
+    _say("case:", case)
+    gen = synth.generate_workload(w, workers=1)
+    for mode in w.modes if len(w.modes) > 1 else (0, 1):
+        out = _run(w, _upload(gen), mode)
+        S_ref = _full_check(w, gen, out)
+        _select_checks(w, gen, out, S_ref, [(l, h) for l in range(L) for h in range(H)], mode)
+
+
+def test_zero_queries_closed_form():
+    w = synth.LLAMA8B_8K.shrink(n_c=1500, n_prompt=9, L=1, H=2)
+    gen = synth.generate_workload(w, workers=1)
+    gen["q"][:] = 0
+    out = _run(w, _upload(gen))
+    n_in = w.n_in
+    lse = out["lse"].cpu().numpy()
+    want = np.log(w.n_c + np.arange(n_in) + 1.0)
+    for l in range(w.L):
+        for h in range(w.H):
+            for g in range(w.G):
+                check_lse(lse[l, h, g], want)
+    check_scores(out["scores"].cpu().numpy(), np.full((1, 2, w.n_c), 1.0 / (w.n_c + 1)))
+
+
+def test_keep_all_is_identity():
+    w = synth.TINY.shrink(keep_ratio=1.0, L=2, H=2, n_c=300)
+    gen = synth.generate_workload(w, workers=1)
+    for mode in (0, 1):
+        out = _run(w, _upload(gen), mode)
+        assert np.array_equal(out["idx"].cpu().numpy(), np.tile(np.arange(300), 4))
+        assert np.array_equal(out["offsets"].cpu().numpy(), np.arange(5) * 300)
+        assert np.array_equal(dev_bf16_bits(out["k_out"]), gen["k_ctx"].reshape(-1, w.d))
+        assert np.array_equal(dev_bf16_bits(out["v_out"]), gen["v_ctx"].reshape(-1, w.d))
+
+
+@pytest.mark.parametrize("n_c,L,H", [(5000, 2, 3), (20000, 1, 2), (8193, 2, 1), (1, 3, 2), (7, 1, 4)])
+def test_select_ties_bit_exact(n_c, L, H):
+    rng = np.random.default_rng(n_c + L + H)
+    # few distinct values: long runs of exact ties across chunk boundaries
+    s = (rng.integers(0, 6, size=(L, H, n_c)).astype(np.float32) / 8.0)
+    s[0, 0, :min(n_c, 3)] = 0.0
+    dev = torch.from_numpy(s).cuda()
+    for mode in (0, 1):
+        for r in (0.01, 0.1, 0.3, 0.5, 0.77, 1.0):
+            o, i = kvq.kv_topk_select(dev, r, mode)
+            ro, ri = oracle.select(s, r, mode)
+            assert np.array_equal(o.cpu().numpy(), ro), (mode, r)
+            assert np.array_equal(i.cpu().numpy(), ri), (mode, r)
+
+
+def test_select_distinct_bit_patterns():
+    # scores spanning many exponents, including exact zeros and 1.0
+    rng = np.random.default_rng(5)
+    s = np.exp(rng.uniform(-80, 0, size=(3, 2, 3000))).astype(np.float32)
+    s[1, 1, 100:200] = 0.0
+    s[2, 0, 5] = 1.0
+    dev = torch.from_numpy(s).cuda()
+    for mode in (0, 1):
+        for r in (0.001, 0.25, 0.9):
+            o, i = kvq.kv_topk_select(dev, r, mode)
+            ro, ri = oracle.select(s, r, mode)
+            assert np.array_equal(o.cpu().numpy(), ro)
+            assert np.array_equal(i.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_compact_given_indices(d):
+    rng = np.random.default_rng(d)
+    L, H, n_c = 3, 2, 700
+    k = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
+    v = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
+    counts = rng.integers(0, 200, size=L * H)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    idx = np.concatenate([np.sort(rng.choice(n_c, size=c, replace=False)) for c in counts]).astype(np.int32)
+    ko, vo = kvq.kv_compact(to_dev_bf16(k), to_dev_bf16(v), torch.from_numpy(off).cuda(),
+                            torch.from_numpy(idx).cuda())
+    rko, rvo = oracle.compact(k, v, off, idx)
+    assert np.array_equal(dev_bf16_bits(ko), rko)
+    assert np.array_equal(dev_bf16_bits(vo), rvo)
+    # indices outside [0, n_c) give zero rows (documented), never a stray read
+    bad = idx.copy()
+    bad[:: 7] = -1
+    bad[3:: 11] = n_c
+    ko, vo = kvq.kv_compact(to_dev_bf16(k), to_dev_bf16(v), torch.from_numpy(off).cuda(),
+                            torch.from_numpy(bad).cuda())
+    got = dev_bf16_bits(ko)
+    zero = (bad < 0) | (bad >= n_c)
+    assert np.all(got[zero] == 0)
+    assert np.array_equal(got[~zero], rko[~zero])
+
+
+def test_deterministic_reruns():
+    w = synth.LLAMA8B_8K.shrink(n_c=3000, n_prompt=32, L=2, H=2)
+    gen = synth.generate_workload(w, workers=1)
+    dev = _upload(gen)
+    a = _run(w, dev)
+    b = _run(w, dev)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, launched exactly as the benchmark launches them
+# ---------------------------------------------------------------------------
+def _sampled_select_checks(w, out, S_ref, heads):
+    """Band rule on the GPU-score selection, and bit-exact selection of the
+    oracle's own (fp32-rounded) scores, for each sampled head."""
+    off = out["offsets"].cpu().numpy()
+    idx = out["idx"].cpu().numpy()
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    for (l, h) in heads:
+        band = check_topk_band(head_kept(off, idx, l * w.H + h), S_ref[l, h], k)
+        _say(f"head ({l},{h}): near-tie band holds {band} keys")
+        s32 = S_ref[l, h].astype(np.float32)[None, None]
+        o2, i2 = kvq.kv_topk_select(torch.from_numpy(s32).cuda(), w.keep_ratio, 0)
+        ro, ri = oracle.select(s32, w.keep_ratio, 0)
+        assert np.array_equal(o2.cpu().numpy(), ro) and np.array_equal(i2.cpu().numpy(), ri)
+
+
+def test_llama8b_8k_full_size():
+    w = synth.LLAMA8B_8K
+    _say("case: full", w.name)
+    gen = synth.generate_workload(w, workers=WORKERS)
+    out = _run(w, _upload(gen))
+    heads = [(0, 0), (31, 7), (13, 5)]
+    S_ref = _full_check(w, gen, out, heads)
+    _sampled_select_checks(w, out, S_ref, heads)
+    # every head: k ascending positions in range; compacted rows are the kept rows
+    off = out["offsets"].cpu().numpy()
+    idx = out["idx"].cpu().numpy()
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    assert np.array_equal(off, np.arange(w.heads + 1) * k)
+    per = idx.reshape(w.heads, k)
+    assert np.all(np.diff(per, axis=1) > 0) and per.min() >= 0 and per.max() < w.n_c
+    ko = dev_bf16_bits(out["k_out"]).reshape(w.heads, k, w.d)
+    vo = dev_bf16_bits(out["v_out"]).reshape(w.heads, k, w.d)
+    kc = gen["k_ctx"].reshape(w.heads, w.n_c, w.d)
+    vc = gen["v_ctx"].reshape(w.heads, w.n_c, w.d)
+    for lh in (0, 77, 255):
+        assert np.array_equal(ko[lh], kc[lh][per[lh]])
+        assert np.array_equal(vo[lh], vc[lh][per[lh]])
+    # full-size compaction of an index set the oracle made, bit-exact
+    rng = np.random.default_rng(7)
+    ridx = np.concatenate([np.sort(rng.choice(w.n_c, size=k, replace=False))
+                           for _ in range(w.heads)]).astype(np.int32)
+    roff = (np.arange(w.heads + 1) * k).astype(np.int64)
+    ko2, vo2 = kvq.kv_compact(to_dev_bf16(gen["k_ctx"]), to_dev_bf16(gen["v_ctx"]),
+                              torch.from_numpy(roff).cuda(), torch.from_numpy(ridx).cuda())
+    rko, rvo = oracle.compact(gen["k_ctx"], gen["v_ctx"], roff, ridx)
+    assert np.array_equal(dev_bf16_bits(ko2), rko)
+    assert np.array_equal(dev_bf16_bits(vo2), rvo)
