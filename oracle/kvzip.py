@@ -125,41 +125,33 @@ def row_lse(q_row: np.ndarray, i: int, k_ctx: np.ndarray, k_new: np.ndarray,
 
 
 # ----------------------------------------------------------------------------
-# parallel driver over row blocks of one head (fork pool, one BLAS thread each)
+# parallel driver over row blocks of one head (threads, one BLAS thread each)
 # ----------------------------------------------------------------------------
-_SHARED = {}
-
-
-def _block_job(args):
-    g, i0, i1 = args
-    q, k_all, n_c, scale = (_SHARED[k] for k in ("q", "k_all", "n_c", "scale"))
-    a, l = attention_rows(q[g, i0:i1], np.arange(i0, i1), k_all, n_c, scale)
-    return g, i0, i1, l, a[:, :n_c].max(axis=0)
-
-
 def head_scores_parallel(q, k_ctx, k_new, scale, workers: int,
                          row_block: int = 128):
-    """Same result as head_scores, split by row blocks over a process pool.
-    The max-combine is exact and order-free, so the result is identical."""
-    import multiprocessing as mp
+    """Same result as head_scores, split by row blocks over a thread pool
+    (NumPy and BLAS release the GIL; nothing is forked).  The max-combine is
+    exact and order-free, so the result is identical."""
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
 
     G, n_in, _ = q.shape
     n_c = k_ctx.shape[0]
-    _SHARED.update(q=q, k_all=np.concatenate([k_ctx, k_new], axis=0),
-                   n_c=n_c, scale=scale)
+    k_all = np.concatenate([k_ctx, k_new], axis=0)
     jobs = [(g, i0, min(n_in, i0 + row_block))
             for g in range(G) for i0 in range(0, n_in, row_block)]
-    S = np.zeros(n_c)
     lse = np.empty((G, n_in))
-    try:
-        with threadpool_limits(limits=1):
-            with mp.get_context("fork").Pool(workers) as pool:
-                for g, i0, i1, l, smax in pool.imap_unordered(_block_job, jobs):
-                    lse[g, i0:i1] = l
-                    np.maximum(S, smax, out=S)
-    finally:
-        _SHARED.clear()
+    S = np.zeros(n_c)
+
+    def block(job):
+        g, i0, i1 = job
+        a, l = attention_rows(q[g, i0:i1], np.arange(i0, i1), k_all, n_c, scale)
+        lse[g, i0:i1] = l
+        return a[:, :n_c].max(axis=0)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max(1, workers)) as ex:
+        for smax in ex.map(block, jobs):
+            np.maximum(S, smax, out=S)
     return S, lse
 
 

@@ -28,6 +28,9 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-op accumulators in ordinary VGPRs: the softmax reductions read
+    # them directly instead of copying them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -16,6 +16,9 @@
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
 //    its rows, so the matrix op itself yields q.k - lse / scale; each lane
 //    holds 16 rows of one key and keeps a lane-local running max.
+//  * The loop is software-pipelined: the next subtile's operands are read
+//    from LDS and the previous subtile's products reduced while the matrix
+//    cores work on the current one.
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
@@ -98,46 +101,70 @@ __global__ __launch_bounds__(256) void colmax_kernel(
 
   float M[2] = {-__builtin_inff(), -__builtin_inff()};
 
+  // operands of one 32-row subtile: the query rows (A) and their seeds
+  struct Sub {
+    bf16x8 a[C::KS];
+    f32x16 init;
+  };
+  auto read_sub = [&](int buf, int sub, Sub& o) {
+    const uint16_t* arow =
+        &sq[buf][(sub * 32 + (lane & 31)) * C::ST + 8 * (lane >> 5)];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      o.a[s] = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
+    // seed: -lse / scale of the 16 rows this lane holds
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(
+          &snl[buf][sub * 32 + 8 * grp + 4 * (lane >> 5)]);
+      o.init[4 * grp + 0] = v[0];
+      o.init[4 * grp + 1] = v[1];
+      o.init[4 * grp + 2] = v[2];
+      o.init[4 * grp + 3] = v[3];
+    }
+  };
+  auto reduce2 = [&](const f32x16& x0, const f32x16& x1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      M[0] = max3f(M[0], x0[4 * u], max3f(x0[4 * u + 1], x0[4 * u + 2], x0[4 * u + 3]));
+      M[1] = max3f(M[1], x1[4 * u], max3f(x1[4 * u + 1], x1[4 * u + 2], x1[4 * u + 3]));
+    }
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
+  // software pipeline: operands of the next subtile are read from LDS and
+  // the previous subtile's results reduced while the matrix cores run
+  f32x16 p0, p1;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
+
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
     if (t + 1 < T) load_tile(t + 1);
-
+    Sub cur;
+    read_sub(buf, 0, cur);
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub) {
-      // seed: -lse / scale of the 16 rows this lane holds
-      f32x16 init;
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(
-            &snl[buf][sub * 32 + 8 * grp + 4 * (lane >> 5)]);
-        init[4 * grp + 0] = v[0];
-        init[4 * grp + 1] = v[1];
-        init[4 * grp + 2] = v[2];
-        init[4 * grp + 3] = v[3];
-      }
-      f32x16 acc0 = init, acc1 = init;
-      const uint16_t* arow =
-          &sq[buf][(sub * 32 + (lane & 31)) * C::ST + 8 * (lane >> 5)];
+      Sub nxt;
+      if (sub + 1 < C::NSUB) read_sub(buf, sub + 1, nxt);
+      f32x16 c0 = cur.init, c1 = cur.init;
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
-        acc0 = mfma32(a, bk[0][s], acc0);
-        acc1 = mfma32(a, bk[1][s], acc1);
+        c0 = mfma32(cur.a[s], bk[0][s], c0);
+        c1 = mfma32(cur.a[s], bk[1][s], c1);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        M[0] = max3f(M[0], acc0[4 * u], max3f(acc0[4 * u + 1], acc0[4 * u + 2], acc0[4 * u + 3]));
-        M[1] = max3f(M[1], acc1[4 * u], max3f(acc1[4 * u + 1], acc1[4 * u + 2], acc1[4 * u + 3]));
-      }
+      reduce2(p0, p1);
+      p0 = c0;
+      p1 = c1;
+      if (sub + 1 < C::NSUB) cur = nxt;
     }
-
     if (t + 1 < T) store_tile(buf ^ 1);
     __syncthreads();
   }
+  reduce2(p0, p1);
 
 #pragma unroll
   for (int f = 0; f < 2; ++f) {

@@ -17,7 +17,11 @@
 //    A operand and the queries as B, so each lane holds 16 keys of one query:
 //    the running max and sum of the online softmax stay lane-local; the two
 //    half-waves that share a query merge once at the end.
-//  * exp is taken as exp2 with the scale folded into one FMA per logit.
+//  * exp is taken as exp2 with the scale folded into one FMA per logit; the
+//    running max is updated lazily (see below), so the hot path has no
+//    per-logit max, and masked keys enter as a -inf accumulator seed.
+//  * The loop is software-pipelined by one 32-key subtile so the matrix
+//    cores and the VALU/transcendental units work at the same time.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -112,42 +116,81 @@ __global__ __launch_bounds__(256) void lse_kernel(
     }
   };
 
+  // Online normaliser per lane and fragment: the lane's keys contribute
+  // sum * 2^(m * c2) (raw-dot units).  m is a lazily updated running max: a
+  // subtile is first summed against the current m and only if that sum
+  // exceeds 2^64 (or is not finite: the first real subtile, as m starts at
+  // kNegBig) is m raised to the subtile max and the subtile re-summed.  Sums
+  // stay far from overflow (< 2^64 per subtile) and terms far below m only
+  // underflow where they are negligible, so the result is exact to fp32
+  // rounding while the hot path costs one FMA, one exp2 and one add per logit.
   float m[2] = {kNegBig, kNegBig};
+  float nmc[2] = {-kNegBig * c2, -kNegBig * c2};
   float sum[2] = {0.f, 0.f};
+  constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
 
-  auto update = [&](f32x16 acc, int f, bool masked, int seg, int kbase) {
-    if (masked) {
-      const int qpos = fpos0[f] + (lane & 31);
+  auto accumulate2 = [&](const f32x16& x0, const f32x16& x1) {
+    float e0[16], e1[16];
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int key = kbase + acc_row(a, lane);
-        const bool vis = seg == 0 ? key < n_c : (key <= qpos && key < n_in);
-        acc[a] = vis ? acc[a] : -__builtin_inff();
-      }
+    for (int a = 0; a < 16; ++a) {
+      e0[a] = fast_exp2(__builtin_fmaf(x0[a], c2, nmc[0]));
+      e1[a] = fast_exp2(__builtin_fmaf(x1[a], c2, nmc[1]));
     }
-    float t4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      t4[u] = max3f(acc[4 * u], acc[4 * u + 1],
-                    __builtin_fmaxf(acc[4 * u + 2], acc[4 * u + 3]));
-    const float tmax = max3f(t4[0], t4[1], __builtin_fmaxf(t4[2], t4[3]));
-    const float mn = __builtin_fmaxf(m[f], tmax);
-    sum[f] *= fast_exp2((m[f] - mn) * c2);
-    m[f] = mn;
-    const float nmc = -mn * c2;
-    float p[16];
-#pragma unroll
-    for (int a = 0; a < 16; ++a) p[a] = fast_exp2(__builtin_fmaf(acc[a], c2, nmc));
 #pragma unroll
     for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-      for (int a = 0; a < w; ++a) p[a] += p[a + w];
-    sum[f] += p[0];
+      for (int a = 0; a < w; ++a) {
+        e0[a] += e0[a + w];
+        e1[a] += e1[a + w];
+      }
+    float ts0 = e0[0], ts1 = e1[0];
+    if (!(ts0 <= kRescaleAt) || !(ts1 <= kRescaleAt)) {
+      // rare path: raise the running max to this subtile's max and re-sum
+      const f32x16* xs[2] = {&x0, &x1};
+      float* tsp[2] = {&ts0, &ts1};
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (*tsp[f] <= kRescaleAt) continue;
+        const f32x16& x = *xs[f];
+        float tm = x[0];
+#pragma unroll
+        for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
+        const float mn = __builtin_fmaxf(m[f], tm);
+        sum[f] *= fast_exp2((m[f] - mn) * c2);
+        m[f] = mn;
+        nmc[f] = -mn * c2;
+        float t = 0.f;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc[f]));
+        *tsp[f] = t;
+      }
+    }
+    sum[0] += ts0;
+    sum[1] += ts1;
+  };
+
+  // Accumulator seed: 0 for keys a row sees, -inf for keys it must not see
+  // (cached-key tail past n_c, new keys past the row's position or past n_in).
+  auto seed = [&](int f, int seg, int kbase) {
+    f32x16 init;
+    // last key this lane's row may see within the segment
+    const int qpos = fpos0[f] + (lane & 31);
+    const int lim = (seg == 0 ? n_c - 1 : min(qpos, n_in - 1)) - kbase - 4 * (lane >> 5);
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      init[a] = (8 * (a >> 2) + (a & 3)) <= lim ? 0.f : -__builtin_inff();
+    return init;
   };
 
   load_tile(0);
   store_tile(0);
   __syncthreads();
+
+  // software pipeline: the MFMAs of one 32-key subtile run while the VALU
+  // reduces the previous subtile's logits
+  f32x16 p0, p1;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
 
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
@@ -160,21 +203,30 @@ __global__ __launch_bounds__(256) void lse_kernel(
     const uint16_t* sb = &sk[buf][0];
 #pragma unroll
     for (int sub = 0; sub < C::NSUB; ++sub) {
-      f32x16 acc0 = {}, acc1 = {};
+      f32x16 c0, c1;
+      if (masked) {
+        c0 = seed(0, seg, key0 + sub * 32);
+        c1 = seed(1, seg, key0 + sub * 32);
+      } else {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) c0[a] = c1[a] = 0.f;
+      }
       const uint16_t* arow = sb + (sub * 32 + (lane & 31)) * C::ST + 8 * (lane >> 5);
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
-        acc0 = mfma32(a, bq[0][s], acc0);
-        acc1 = mfma32(a, bq[1][s], acc1);
+        c0 = mfma32(a, bq[0][s], c0);
+        c1 = mfma32(a, bq[1][s], c1);
       }
-      update(acc0, 0, masked, seg, key0 + sub * 32);
-      update(acc1, 1, masked, seg, key0 + sub * 32);
+      accumulate2(p0, p1);
+      p0 = c0;
+      p1 = c1;
     }
 
     if (t + 1 < T) store_tile(buf ^ 1);
     __syncthreads();
   }
+  accumulate2(p0, p1);
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll

@@ -165,7 +165,7 @@ def generate_workload(w: Workload,
                       workers: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Full [L][H]-indexed bf16 bit arrays for the listed heads.
 
-    Heads not listed stay zero.  Uses a process pool when workers > 1.
+    Heads not listed stay zero.  Uses a thread pool when workers > 1.
     """
     parts = tuple(parts)
     if heads is None:
@@ -179,16 +179,20 @@ def generate_workload(w: Workload,
     out = {p: np.zeros(shapes[p], dtype=np.uint16) for p in parts}
     jobs = [(w, l, h, parts) for (l, h) in heads]
     workers = default_workers() if workers is None else workers
+
+    def run(job):
+        l, h, d = _head_job(job)
+        for p in parts:
+            out[p][l, h] = d[p]
+
     if workers <= 1 or len(jobs) <= 1:
-        results = map(_head_job, jobs)
-        for l, h, d in results:
-            for p in parts:
-                out[p][l, h] = d[p]
+        for job in jobs:
+            run(job)
     else:
-        import multiprocessing as mp
-        ctx = mp.get_context("fork")
-        with ctx.Pool(min(workers, len(jobs))) as pool:
-            for l, h, d in pool.imap_unordered(_head_job, jobs, chunksize=1):
-                for p in parts:
-                    out[p][l, h] = d[p]
+        # threads, not processes: NumPy's random fills, BLAS and ufunc loops
+        # release the GIL, and nothing is forked (safe after GPU start-up)
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1), ThreadPoolExecutor(min(workers, len(jobs))) as ex:
+            list(ex.map(run, jobs))
     return out
