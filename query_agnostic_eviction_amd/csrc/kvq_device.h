@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -58,5 +60,56 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
   const int q = nblocks / kXcds, r = nblocks % kXcds;
   return xcd * q + (xcd < r ? xcd : r) + bid / kXcds;
 }
+
+// A tile of bf16 rows of length D in LDS, 32 KB per buffer, filled straight
+// from global memory by 16-byte LDS-DMA loads (global_load_lds_dwordx4: each
+// wave instruction writes 64 x 16 B contiguously, so no register staging and
+// no LDS store instructions are needed).
+//
+// Layout: row r occupies elements [r*D, (r+1)*D); its 16-byte chunk c is
+// stored in chunk slot c ^ swz(r).  The matrix-operand reads take 16 bytes of
+// one row per lane, 32 rows at a time; the XOR spreads 16 consecutive rows of
+// the same chunk over distinct LDS banks, so those reads are conflict-free
+// without padding (padding is impossible with contiguous DMA writes).
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROWS = 16384 / D;            // 32 KB of bf16 per buffer
+  static constexpr int ELEMS = ROWS * D;
+  static constexpr int LOADS = ROWS * CPR / 256;    // 16-B loads per thread (256 threads)
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 64 ? ((r >> 1) & 7) : (r & 15);
+  }
+  // element offset, within a tile, of the load slot (i, tid) and the global
+  // element offset (relative to the tile's first row) it must fetch
+  __device__ static __forceinline__ int src_rel(int i, int tid) {
+    const int s = i * 256 + tid;
+    const int r = s / CPR, p = s % CPR;
+    return r * D + ((p ^ swz(r)) * 8);
+  }
+  __device__ static __forceinline__ int src_row(int i, int tid) {
+    return (i * 256 + tid) / CPR;
+  }
+  // element offset of the 16 B lane l reads for k-step s of a 32-row block
+  // starting at row 0 (add 32 * D per further block)
+  __device__ static __forceinline__ int read_off(int lane, int s) {
+    const int r = lane & 31;
+    const int c = 2 * s + (lane >> 5);
+    return r * D + ((c ^ swz(r)) * 8);
+  }
+};
+
+// 16-byte global -> LDS copy; `lds` must be the same for the whole wave (the
+// lane's data lands at lds + 16 * lane).
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds, 16, 0, 0);
+}
+// 4-byte global -> LDS copy; the lane's data lands at lds + 4 * lane.
+__device__ __forceinline__ void lds_dma4(const void* gsrc, void* lds) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds, 4, 0, 0);
+}
+
+// Wait for this wave's outstanding memory operations (incl. LDS-DMA).
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace kvq

@@ -72,21 +72,23 @@ __global__ __launch_bounds__(256) void colmax_kernel(
 
   u32x4 pre[C::LDPT];
   float pre_nl = 0.f;
+  bool pre_ok = false;
   auto load_tile = [&](int t) {
     const int r0 = t * C::QT;
 #pragma unroll
     for (int it = 0; it < C::LDPT; ++it) {
       const int c = tid + it * 256;
       const int row = c / C::CPR, col = c % C::CPR;
-      // branch-free tail: read the last valid row, then zero it
+      // past the last row re-read it: finite values, and the -inf seed of
+      // a padding row keeps it out of the max.  Nothing here touches the
+      // loaded data, so the loads stay in flight across the compute.
       const int r = r0 + row;
-      const uint32_t keep = r < R ? 0xffffffffu : 0u;
-      pre[it] = ldg16(qh + (size_t)(r < R ? r : R - 1) * D + col * 8) & keep;
+      pre[it] = ldg16(qh + (size_t)(r < R ? r : R - 1) * D + col * 8);
     }
     if (tid < C::QT) {
       const int r = r0 + tid;
-      const float v = -lh_lse[r < R ? r : R - 1] * inv_scale;
-      pre_nl = r < R ? v : -__builtin_inff();  // padding rows never win the max
+      pre_nl = lh_lse[r < R ? r : R - 1];
+      pre_ok = r < R;
     }
   };
   auto store_tile = [&](int buf) {
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(
       const int row = c / C::CPR, col = c % C::CPR;
       *reinterpret_cast<u32x4*>(&sq[buf][row * C::ST + col * 8]) = pre[it];
     }
-    if (tid < C::QT) snl[buf][tid] = pre_nl;
+    if (tid < C::QT) snl[buf][tid] = pre_ok ? -pre_nl * inv_scale : -__builtin_inff();
   };
 
   float M[2] = {-__builtin_inff(), -__builtin_inff()};

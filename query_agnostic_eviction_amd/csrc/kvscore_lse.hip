@@ -10,15 +10,16 @@
 //    fragment is 32 consecutive positions of one query head g; fragments of a
 //    head are numbered b * G + g over 32-position blocks b).  Each wave keeps
 //    its two fragments' queries in registers for the whole key sweep.
-//  * Keys stream through LDS in tiles of KT rows (double-buffered, one
-//    barrier per tile): first the cached keys, then the new keys up to the
-//    workgroup's last position.
+//  * Keys stream through LDS in 32 KB tiles (16384 / d keys), double-buffered
+//    and filled by LDS-DMA straight from HBM while the previous tile is in
+//    use: first the cached keys, then the new keys up to the workgroup's last
+//    position.  One barrier per tile.
 //  * Logits come from the 32x32x16 bf16 matrix op with the key tile as the
 //    A operand and the queries as B, so each lane holds 16 keys of one query:
-//    the running max and sum of the online softmax stay lane-local; the two
-//    half-waves that share a query merge once at the end.
+//    the softmax sums stay lane-local; the two half-waves that share a query
+//    merge once at the end.
 //  * exp is taken as exp2 with the scale folded into one FMA per logit; the
-//    running max is updated lazily (see below), so the hot path has no
+//    running max is updated lazily (see accumulate2), so the hot path has no
 //    per-logit max, and masked keys enter as a -inf accumulator seed.
 //  * The loop is software-pipelined by one 32-key subtile so the matrix
 //    cores and the VALU/transcendental units work at the same time.
@@ -32,22 +33,20 @@ constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxi
 
 template <int D>
 struct LseCfg {
-  static constexpr int KT = (D == 256) ? 32 : 64;  // keys per LDS tile
-  static constexpr int NSUB = KT / 32;
-  static constexpr int KS = D / 16;                // k-steps of the 32x32x16 op
-  static constexpr int ST = D + 8;                 // LDS row stride (bf16), +16 B pad
-  static constexpr int CPR = D / 8;                // 16-byte chunks per key row
-  static constexpr int LDPT = KT * CPR / 256;      // chunks per thread per tile
+  static constexpr int KT = Tile<D>::ROWS;  // keys per tile
+  static constexpr int NSUB = KT / 32;      // 32-key subtiles per tile
+  static constexpr int KS = D / 16;         // k-steps of the 32x32x16 op
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void lse_kernel(
+__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ k_new, float* __restrict__ lse, int G,
     int n_c, int n_in, int nfrag_head, int wg_per_head, float c2,
     float scale) {
   using C = LseCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][C::KT * C::ST];
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[2 * TL::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -91,28 +90,33 @@ __global__ __launch_bounds__(256) void lse_kernel(
   const int T1 = (new_len + C::KT - 1) / C::KT;
   const int T = T0 + T1;
 
-  u32x4 pre[C::LDPT];
-  auto load_tile = [&](int t) {
+  // per-thread constant parts of the tile loads and of the operand reads
+  int src_rel[TL::LOADS];
+#pragma unroll
+  for (int i = 0; i < TL::LOADS; ++i) src_rel[i] = TL::src_rel(i, tid);
+  int rd_off[C::KS];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) rd_off[s] = TL::read_off(lane, s);
+
+  // LDS-DMA of tile t into buffer `buf`; rows past the segment end re-read
+  // its last row (finite values; those keys are masked by the -inf seed)
+  auto issue_tile = [&](int t, int buf) {
     const int seg = t < T0 ? 0 : 1;
     const int key0 = (seg == 0 ? t : t - T0) * C::KT;
     const int len = seg == 0 ? n_c : new_len;
+    const uint16_t* base = seg_ptr[seg] + (size_t)key0 * D;
+    uint16_t* dst = sk + buf * TL::ELEMS + wave * 64 * 8;
+    if (key0 + C::KT <= len) {
 #pragma unroll
-    for (int it = 0; it < C::LDPT; ++it) {
-      const int c = tid + it * 256;
-      const int row = c / C::CPR, col = c % C::CPR;
-      const int key = key0 + row;
-      // branch-free tail: read the last valid row, then zero it
-      const int kc = key < len ? key : len - 1;
-      const uint32_t keep = key < len ? 0xffffffffu : 0u;
-      pre[it] = ldg16(seg_ptr[seg] + (size_t)kc * D + col * 8) & keep;
-    }
-  };
-  auto store_tile = [&](int buf) {
+      for (int i = 0; i < TL::LOADS; ++i) lds_dma16(base + src_rel[i], dst + i * 256 * 8);
+    } else {
+      const int last = len - 1 - key0;
 #pragma unroll
-    for (int it = 0; it < C::LDPT; ++it) {
-      const int c = tid + it * 256;
-      const int row = c / C::CPR, col = c % C::CPR;
-      *reinterpret_cast<u32x4*>(&sk[buf][row * C::ST + col * 8]) = pre[it];
+      for (int i = 0; i < TL::LOADS; ++i) {
+        const int r = TL::src_row(i, tid);
+        const int rel = src_rel[i] - (r > last ? (r - last) * D : 0);
+        lds_dma16(base + rel, dst + i * 256 * 8);
+      }
     }
   };
 
@@ -130,20 +134,20 @@ __global__ __launch_bounds__(256) void lse_kernel(
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
 
   auto accumulate2 = [&](const f32x16& x0, const f32x16& x1) {
-    float e0[16], e1[16];
+    // four running partial sums per fragment keep few temporaries live
+    float e0[4], e1[4];
 #pragma unroll
-    for (int a = 0; a < 16; ++a) {
+    for (int a = 0; a < 4; ++a) {
       e0[a] = fast_exp2(__builtin_fmaf(x0[a], c2, nmc[0]));
       e1[a] = fast_exp2(__builtin_fmaf(x1[a], c2, nmc[1]));
     }
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int a = 0; a < w; ++a) {
-        e0[a] += e0[a + w];
-        e1[a] += e1[a + w];
-      }
-    float ts0 = e0[0], ts1 = e1[0];
+    for (int a = 4; a < 16; ++a) {
+      e0[a & 3] += fast_exp2(__builtin_fmaf(x0[a], c2, nmc[0]));
+      e1[a & 3] += fast_exp2(__builtin_fmaf(x1[a], c2, nmc[1]));
+    }
+    float ts0 = (e0[0] + e0[1]) + (e0[2] + e0[3]);
+    float ts1 = (e1[0] + e1[1]) + (e1[2] + e1[3]);
     if (!(ts0 <= kRescaleAt) || !(ts1 <= kRescaleAt)) {
       // rare path: raise the running max to this subtile's max and re-sum
       const f32x16* xs[2] = {&x0, &x1};
@@ -182,49 +186,63 @@ __global__ __launch_bounds__(256) void lse_kernel(
     return init;
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
   // software pipeline: the MFMAs of one 32-key subtile run while the VALU
   // reduces the previous subtile's logits
   f32x16 p0, p1;
 #pragma unroll
   for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
 
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
+  // one 32-key subtile; unmasked subtiles start the chain from an inline zero
+  auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase) {
+    f32x16 c0, c1;
+    if (masked) {
+      c0 = seed(0, seg, kbase);
+      c1 = seed(1, seg, kbase);
+    } else {
+      const f32x16 z = {};
+      c0 = z;
+      c1 = z;
+    }
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
+      c0 = mfma32(a, bq[0][s], c0);
+      c1 = mfma32(a, bq[1][s], c1);
+    }
+    accumulate2(p0, p1);
+    p0 = c0;
+    p1 = c1;
+  };
 
+  // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
+  // t, then wait for the prefetch and publish it with one barrier
+  auto step = [&](int t, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (t + 1 < T) issue_tile(t + 1, BUF ^ 1);
     const int seg = t < T0 ? 0 : 1;
     const int key0 = (seg == 0 ? t : t - T0) * C::KT;
     const bool masked = seg == 0 ? (key0 + C::KT > n_c)
                                  : (key0 + C::KT - 1 > pos_min || key0 + C::KT > n_in);
-    const uint16_t* sb = &sk[buf][0];
+    const uint16_t* sb = sk + BUF * TL::ELEMS;
+    if (masked) {
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      f32x16 c0, c1;
-      if (masked) {
-        c0 = seed(0, seg, key0 + sub * 32);
-        c1 = seed(1, seg, key0 + sub * 32);
-      } else {
+      for (int sub = 0; sub < C::NSUB; ++sub)
+        subtile(sb + sub * 32 * D, true, seg, key0 + sub * 32);
+    } else {
 #pragma unroll
-        for (int a = 0; a < 16; ++a) c0[a] = c1[a] = 0.f;
-      }
-      const uint16_t* arow = sb + (sub * 32 + (lane & 31)) * C::ST + 8 * (lane >> 5);
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
-        c0 = mfma32(a, bq[0][s], c0);
-        c1 = mfma32(a, bq[1][s], c1);
-      }
-      accumulate2(p0, p1);
-      p0 = c0;
-      p1 = c1;
+      for (int sub = 0; sub < C::NSUB; ++sub)
+        subtile(sb + sub * 32 * D, false, seg, key0 + sub * 32);
     }
-
-    if (t + 1 < T) store_tile(buf ^ 1);
+    wait_all_mem();
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  wait_all_mem();
+  __syncthreads();
+  for (int t = 0; t < T; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
   accumulate2(p0, p1);
 
