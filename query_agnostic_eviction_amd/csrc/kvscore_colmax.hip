@@ -12,13 +12,13 @@
 // Mapping on gfx950:
 //  * A workgroup of 4 waves owns 256 cached keys (2 fragments of 32 per
 //    wave, kept in registers as the B operand); it sweeps all G * n_in query
-//    rows of its head, staged through LDS in double-buffered tiles.
+//    rows of its head in 32 KB tiles (16384 / d rows), double-buffered and
+//    filled by LDS-DMA straight from HBM together with the rows' lse.
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
 //    its rows, so the matrix op itself yields q.k - lse / scale; each lane
 //    holds 16 rows of one key and keeps a lane-local running max.
-//  * The loop is software-pipelined: the next subtile's operands are read
-//    from LDS and the previous subtile's products reduced while the matrix
-//    cores work on the current one.
+//  * The loop is software-pipelined: the previous subtile's products are
+//    reduced while the matrix cores work on the current one.
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
@@ -29,22 +29,21 @@ namespace {
 
 template <int D>
 struct ColCfg {
-  static constexpr int QT = (D == 256) ? 32 : 64;  // query rows per LDS tile
+  static constexpr int QT = Tile<D>::ROWS;  // query rows per tile
   static constexpr int NSUB = QT / 32;
   static constexpr int KS = D / 16;
-  static constexpr int ST = D + 8;
-  static constexpr int CPR = D / 8;
-  static constexpr int LDPT = QT * CPR / 256;
+  static constexpr int LSE_LOADS = QT / 64;  // 4-byte DMA instructions per tile
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void colmax_kernel(
+__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const float* __restrict__ lse, float* __restrict__ scores, int G, int n_c,
     int n_in, int wg_per_head, float c2, float inv_scale) {
   using C = ColCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[2][C::QT * C::ST];
-  __shared__ __attribute__((aligned(16))) float snl[2][C::QT];
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t sq[2 * TL::ELEMS];
+  __shared__ __attribute__((aligned(1024))) float sl[2 * C::QT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -70,61 +69,40 @@ __global__ __launch_bounds__(256) void colmax_kernel(
   const float* lh_lse = lse + (size_t)lh * R;
   const int T = (R + C::QT - 1) / C::QT;
 
-  u32x4 pre[C::LDPT];
-  float pre_nl = 0.f;
-  bool pre_ok = false;
-  auto load_tile = [&](int t) {
+  int src_rel[TL::LOADS];
+#pragma unroll
+  for (int i = 0; i < TL::LOADS; ++i) src_rel[i] = TL::src_rel(i, tid);
+  int rd_off[C::KS];
+#pragma unroll
+  for (int s = 0; s < C::KS; ++s) rd_off[s] = TL::read_off(lane, s);
+
+  // LDS-DMA of tile t (query rows and their lse) into buffer `buf`; rows
+  // past R re-read row R-1 (finite values; their seed is -inf)
+  auto issue_tile = [&](int t, int buf) {
     const int r0 = t * C::QT;
+    const uint16_t* base = qh + (size_t)r0 * D;
+    uint16_t* dst = sq + buf * TL::ELEMS + wave * 64 * 8;
+    if (r0 + C::QT <= R) {
 #pragma unroll
-    for (int it = 0; it < C::LDPT; ++it) {
-      const int c = tid + it * 256;
-      const int row = c / C::CPR, col = c % C::CPR;
-      // past the last row re-read it: finite values, and the -inf seed of
-      // a padding row keeps it out of the max.  Nothing here touches the
-      // loaded data, so the loads stay in flight across the compute.
-      const int r = r0 + row;
-      pre[it] = ldg16(qh + (size_t)(r < R ? r : R - 1) * D + col * 8);
-    }
-    if (tid < C::QT) {
-      const int r = r0 + tid;
-      pre_nl = lh_lse[r < R ? r : R - 1];
-      pre_ok = r < R;
-    }
-  };
-  auto store_tile = [&](int buf) {
+      for (int i = 0; i < TL::LOADS; ++i) lds_dma16(base + src_rel[i], dst + i * 256 * 8);
+      if (wave < C::LSE_LOADS)
+        lds_dma4(lh_lse + r0 + wave * 64 + lane, sl + buf * C::QT + wave * 64);
+    } else {
+      const int last = R - 1 - r0;
 #pragma unroll
-    for (int it = 0; it < C::LDPT; ++it) {
-      const int c = tid + it * 256;
-      const int row = c / C::CPR, col = c % C::CPR;
-      *reinterpret_cast<u32x4*>(&sq[buf][row * C::ST + col * 8]) = pre[it];
+      for (int i = 0; i < TL::LOADS; ++i) {
+        const int r = TL::src_row(i, tid);
+        const int rel = src_rel[i] - (r > last ? (r - last) * D : 0);
+        lds_dma16(base + rel, dst + i * 256 * 8);
+      }
+      if (wave < C::LSE_LOADS) {
+        const int r = wave * 64 + lane;
+        lds_dma4(lh_lse + r0 + (r > last ? last : r), sl + buf * C::QT + wave * 64);
+      }
     }
-    if (tid < C::QT) snl[buf][tid] = pre_ok ? -pre_nl * inv_scale : -__builtin_inff();
   };
 
   float M[2] = {-__builtin_inff(), -__builtin_inff()};
-
-  // operands of one 32-row subtile: the query rows (A) and their seeds
-  struct Sub {
-    bf16x8 a[C::KS];
-    f32x16 init;
-  };
-  auto read_sub = [&](int buf, int sub, Sub& o) {
-    const uint16_t* arow =
-        &sq[buf][(sub * 32 + (lane & 31)) * C::ST + 8 * (lane >> 5)];
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      o.a[s] = *reinterpret_cast<const bf16x8*>(arow + 16 * s);
-    // seed: -lse / scale of the 16 rows this lane holds
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(
-          &snl[buf][sub * 32 + 8 * grp + 4 * (lane >> 5)]);
-      o.init[4 * grp + 0] = v[0];
-      o.init[4 * grp + 1] = v[1];
-      o.init[4 * grp + 2] = v[2];
-      o.init[4 * grp + 3] = v[3];
-    }
-  };
   auto reduce2 = [&](const f32x16& x0, const f32x16& x1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -133,38 +111,63 @@ __global__ __launch_bounds__(256) void colmax_kernel(
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  // software pipeline: operands of the next subtile are read from LDS and
-  // the previous subtile's results reduced while the matrix cores run
   f32x16 p0, p1;
 #pragma unroll
   for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
 
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T) load_tile(t + 1);
-    Sub cur;
-    read_sub(buf, 0, cur);
+  // one 32-row subtile: seed with -lse/scale of the lane's 16 rows (-inf
+  // for rows past R), run the products, reduce the previous subtile
+  auto subtile = [&](const uint16_t* sb, const float* slb, bool partial, int rbase) {
+    f32x16 init;
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) {
-      Sub nxt;
-      if (sub + 1 < C::NSUB) read_sub(buf, sub + 1, nxt);
-      f32x16 c0 = cur.init, c1 = cur.init;
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(slb + 8 * grp + 4 * (lane >> 5));
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        c0 = mfma32(cur.a[s], bk[0][s], c0);
-        c1 = mfma32(cur.a[s], bk[1][s], c1);
-      }
-      reduce2(p0, p1);
-      p0 = c0;
-      p1 = c1;
-      if (sub + 1 < C::NSUB) cur = nxt;
+      for (int e = 0; e < 4; ++e) init[4 * grp + e] = -v[e] * inv_scale;
     }
-    if (t + 1 < T) store_tile(buf ^ 1);
+    if (partial) {
+      const int lim = R - 1 - rbase - 4 * (lane >> 5);
+#pragma unroll
+      for (int a = 0; a < 16; ++a)
+        if ((8 * (a >> 2) + (a & 3)) > lim) init[a] = -__builtin_inff();
+    }
+    f32x16 c0 = init, c1 = init;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
+      c0 = mfma32(a, bk[0][s], c0);
+      c1 = mfma32(a, bk[1][s], c1);
+    }
+    reduce2(p0, p1);
+    p0 = c0;
+    p1 = c1;
+  };
+
+  auto step = [&](int t, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (t + 1 < T) issue_tile(t + 1, BUF ^ 1);
+    const int r0 = t * C::QT;
+    const uint16_t* sb = sq + BUF * TL::ELEMS;
+    const float* slb = sl + BUF * C::QT;
+    if (r0 + C::QT <= R) {
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub)
+        subtile(sb + sub * 32 * D, slb + sub * 32, false, r0 + sub * 32);
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub)
+        subtile(sb + sub * 32 * D, slb + sub * 32, true, r0 + sub * 32);
+    }
+    wait_all_mem();
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  wait_all_mem();
+  __syncthreads();
+  for (int t = 0; t < T; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
   reduce2(p0, p1);
 
