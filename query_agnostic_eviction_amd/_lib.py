@@ -24,6 +24,21 @@ EXPORTS = (
 _lib = None
 
 
+def _check_stamp() -> None:
+    """Refuse a library built from other sources than the ones in the tree."""
+    from .build import STAMP, source_digest
+    want = source_digest()
+    try:
+        with open(STAMP) as fh:
+            have = fh.read().strip()
+    except OSError:
+        have = None
+    if have != want:
+        raise ImportError(
+            f"{LIB_PATH} does not match the sources in the tree (stale build): "
+            "rebuild with python -m query_agnostic_eviction_amd.build")
+
+
 def load() -> ctypes.CDLL:
     """Load libkvq.so once; raise if it has not been built."""
     global _lib
@@ -33,6 +48,7 @@ def load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python -m query_agnostic_eviction_amd.build)")
+    _check_stamp()
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                   ctypes.c_float, ctypes.c_double, ctypes.c_size_t)

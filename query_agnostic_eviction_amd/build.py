@@ -8,6 +8,7 @@ instruction selection is disabled for all device code.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -34,6 +35,23 @@ CFLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+def source_digest() -> str:
+    """Digest of everything that determines libkvq.so: sources, header, flags."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(INCLUDE, "kvq.h"), "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(CFLAGS[:-2]).encode())
+    return h.hexdigest()
+
+
+STAMP = LIB + ".stamp"
 
 
 def _hipcc() -> str:
@@ -73,6 +91,8 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as fh:   # lets the loader refuse a stale library
+        fh.write(source_digest() + "\n")
     return LIB
 
 
