@@ -267,3 +267,138 @@ def test_llama8b_8k_full_size():
     rko, rvo = oracle.compact(gen["k_ctx"], gen["v_ctx"], roff, ridx)
     assert np.array_equal(dev_bf16_bits(ko2), rko)
     assert np.array_equal(dev_bf16_bits(vo2), rvo)
+
+
+def _full_size_inputs(w, true_heads, seed=1234):
+    """Device inputs at the workload's full shape: the heads in `true_heads`
+    carry the seeded generator's values, the others cheap seeded GPU noise
+    (same launch configuration; only the listed heads are checked)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    shapes = {"q": (w.G, w.n_in, w.d), "k_ctx": (w.n_c, w.d),
+              "k_new": (w.n_in, w.d), "v_ctx": (w.n_c, w.d)}
+    dev = {}
+    for k, shp in shapes.items():
+        t = torch.empty((w.L, w.H) + shp, dtype=torch.bfloat16, device="cuda")
+        for l in range(w.L):
+            t[l] = torch.randn((w.H,) + shp, generator=g, device="cuda").to(torch.bfloat16)
+        dev[k] = t
+    gens = {}
+    for (l, h) in true_heads:
+        gh = synth.generate_head(w, l, h)
+        gens[(l, h)] = gh
+        for k in shapes:
+            dev[k][l, h] = to_dev_bf16(gh[k])
+    torch.cuda.synchronize()
+    return dev, gens
+
+
+def _check_heads(w, out, gens, heads):
+    lse_g, sc_g = out["lse"], out["scores"]
+    S_ref = {}
+    for (l, h) in heads:
+        _say(f"oracle head ({l},{h}) of {w.name}")
+        S, lse = oracle_head({k: gens[(l, h)][k] for k in ("q", "k_ctx", "k_new")},
+                             float(w.scale), workers=WORKERS)
+        check_lse(lse_g[l, h].cpu().numpy(), lse, f"lse[{l},{h}]")
+        check_scores(sc_g[l, h].cpu().numpy(), S, f"scores[{l},{h}]")
+        S_ref[(l, h)] = S
+    return S_ref
+
+
+def test_qwen14b_32k_full_size():
+    w = synth.QWEN14B_32K
+    heads = [(0, 0), (47, 7)]
+    _say("case: full", w.name)
+    dev, gens = _full_size_inputs(w, heads)
+    out = _run(w, dev)
+    S_ref = _check_heads(w, out, gens, heads)
+    off = out["offsets"].cpu().numpy()
+    idx = out["idx"].cpu().numpy()
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    assert np.array_equal(off, np.arange(w.heads + 1) * k)
+    for (l, h) in heads:
+        lh = l * w.H + h
+        band = check_topk_band(head_kept(off, idx, lh), S_ref[(l, h)], k)
+        _say(f"head ({l},{h}): near-tie band holds {band} keys")
+        s32 = S_ref[(l, h)].astype(np.float32)[None, None]
+        o2, i2 = kvq.kv_topk_select(torch.from_numpy(s32).cuda(), w.keep_ratio, 0)
+        ro, ri = oracle.select(s32, w.keep_ratio, 0)
+        assert np.array_equal(i2.cpu().numpy(), ri)
+        kept = head_kept(off, idx, lh)
+        assert np.array_equal(dev_bf16_bits(out["k_out"][off[lh]:off[lh + 1]]),
+                              gens[(l, h)]["k_ctx"][kept])
+
+
+def test_gemma12b_16k_full_size_both_modes():
+    w = synth.GEMMA12B_16K
+    layer = w.L - 1
+    heads = [(0, 0)] + [(layer, h) for h in range(w.H)]
+    _say("case: full", w.name)
+    dev, gens = _full_size_inputs(w, heads)
+    out0 = _run(w, dev, 0)
+    S_ref = _check_heads(w, out0, gens, heads)
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    off = out0["offsets"].cpu().numpy()
+    idx = out0["idx"].cpu().numpy()
+    for (l, h) in heads:
+        check_topk_band(head_kept(off, idx, l * w.H + h), S_ref[(l, h)], k)
+    # mode 1: one budget over the layer's H * n_c scores
+    sc = out0["scores"]
+    off1, idx1 = kvq.kv_topk_select(sc, w.keep_ratio, 1)
+    off1 = off1.cpu().numpy()
+    idx1 = idx1.cpu().numpy()
+    kl = oracle.keep_count(w.H * w.n_c, w.keep_ratio)
+    assert off1[-1] == w.L * kl
+    lay = np.stack([S_ref[(layer, h)] for h in range(w.H)])        # (H, n_c)
+    flat_kept = np.concatenate([head_kept(off1, idx1, layer * w.H + h) + h * w.n_c
+                                for h in range(w.H)])
+    band = check_topk_band(flat_kept, lay.reshape(-1), kl)
+    _say(f"layer {layer} budget: near-tie band holds {band} keys")
+    # mode 1 on the oracle's own scores: bit-exact
+    s32 = lay.astype(np.float32)[None]
+    o2, i2 = kvq.kv_topk_select(torch.from_numpy(s32).cuda(), w.keep_ratio, 1)
+    ro, ri = oracle.select(s32, w.keep_ratio, 1)
+    assert np.array_equal(o2.cpu().numpy(), ro) and np.array_equal(i2.cpu().numpy(), ri)
+
+
+def test_llama8b_128k_full_size_sampled():
+    w = synth.LLAMA8B_128K
+    l, h = 0, 0
+    _say("case: full", w.name)
+    dev, gens = _full_size_inputs(w, [(l, h)])
+    out = _run(w, dev)
+    gh = gens[(l, h)]
+    q, kc, kn = oracle.workload_head_inputs(gh)
+    lse_g = out["lse"][l, h].cpu().numpy()
+    sc_g = out["scores"][l, h].cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(3)
+    rows = [(g, i) for g in range(w.G) for i in (0, 1, w.n_prompt, w.n_in - 1)]
+    rows += [(int(rng.integers(w.G)), int(rng.integers(w.n_in))) for _ in range(24)]
+    k_all = np.concatenate([kc, kn])
+    for (g, i) in rows:
+        want = oracle.row_lse(q[g, i], i, kc, kn, float(w.scale))
+        check_lse(np.array([lse_g[g, i]]), np.array([want]), f"lse[{g},{i}]")
+        # every score is at least the probability this row gives the key
+        a, _ = oracle.attention_rows(q[g, i][None], np.array([i]), k_all, w.n_c, float(w.scale))
+        p = a[0, :w.n_c]
+        assert np.all(sc_g >= p * (1 - 2e-3) - 1e-6), f"score below row ({g},{i})"
+    assert np.all(sc_g >= 0) and np.all(sc_g <= 1)
+    # exact copies of a key (the repeated spans) receive identical logits in
+    # every row, hence identical scores
+    span = np.arange(64, 128)
+    for kk in (1, 7, 31):
+        assert np.array_equal(sc_g[4096 * kk + span], sc_g[span])
+    # selection: k keys, ascending; the kept set is a valid top-k of the GPU
+    # scores with ties broken toward the lower index
+    off = out["offsets"].cpu().numpy()
+    kept = head_kept(off, out["idx"].cpu().numpy(), 0)
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    assert kept.size == k and np.all(np.diff(kept) > 0)
+    s32 = out["scores"][l, h].cpu().numpy()
+    thr = s32[kept].min()
+    dropped = np.setdiff1d(np.arange(w.n_c), kept)
+    assert s32[dropped].max() <= thr, "a dropped key outscored a kept one"
+    eq = np.flatnonzero(s32 == thr)
+    kept_eq = np.intersect1d(kept, eq)
+    assert np.array_equal(kept_eq, eq[:kept_eq.size]), "ties must go to the lower index"
