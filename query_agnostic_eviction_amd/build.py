@@ -25,6 +25,10 @@ LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvscore_lse.hip", "kvscore_colmax.hip", "kv_topk.hip",
            "kv_compact.hip", "kvq_api.hip"]
 
+# per-source extra flags: pass 2 reduces with max3 on finite values and -inf
+# padding only, so NaN semantics (and their canonicalising copies) are off
+EXTRA_FLAGS = {"kvscore_colmax.hip": ["-fno-honor-nans"]}
+
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -48,6 +52,7 @@ def source_digest() -> str:
     with open(os.path.join(INCLUDE, "kvq.h"), "rb") as fh:
         h.update(fh.read())
     h.update(" ".join(CFLAGS[:-2]).encode())
+    h.update(repr(sorted(EXTRA_FLAGS.items())).encode())
     return h.hexdigest()
 
 
@@ -80,7 +85,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *CFLAGS, *EXTRA_FLAGS.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     workers = max(1, min(len(cmds), os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
         outs = list(ex.map(_run, cmds))

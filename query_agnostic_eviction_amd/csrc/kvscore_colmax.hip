@@ -10,15 +10,16 @@
 // monotone, max_i exp(t_i) = exp(max_i t_i): no per-logit exp is needed.
 //
 // Mapping on gfx950:
-//  * A workgroup of 4 waves owns 256 cached keys (2 fragments of 32 per
+//  * A workgroup of 4 waves owns 384 cached keys (3 fragments of 32 per
 //    wave, kept in registers as the B operand); it sweeps all G * n_in query
 //    rows of its head in 32 KB tiles (16384 / d rows), double-buffered and
 //    filled by LDS-DMA straight from HBM together with the rows' lse.
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
 //    its rows, so the matrix op itself yields q.k - lse / scale; each lane
 //    holds 16 rows of one key and keeps a lane-local running max.
-//  * The loop is software-pipelined: the previous subtile's products are
-//    reduced while the matrix cores work on the current one.
+//  * Each operand read from LDS feeds three matrix ops; the reductions are
+//    max3 on the accumulators (built without NaN semantics, so no
+//    canonicalising copies: inputs are finite and -inf marks padding).
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
@@ -35,6 +36,11 @@ struct ColCfg {
   static constexpr int LSE_LOADS = QT / 64;  // 4-byte DMA instructions per tile
 };
 
+// cached-key fragments of 32 per wave: each operand read from LDS feeds NF
+// matrix ops; 4 waves x NF x 32 keys per workgroup
+constexpr int NF = 3;
+constexpr int kKeysPerWg = 4 * NF * 32;
+
 template <int D>
 __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
@@ -48,14 +54,14 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int lh = logical / wg_per_head;
-  const int j0 = (logical % wg_per_head) * 256;
+  const int j0 = (logical % wg_per_head) * kKeysPerWg;
 
   // this wave's two key fragments -> registers (B operand layout)
-  bf16x8 bk[2][C::KS];
-  int key[2];
+  bf16x8 bk[NF][C::KS];
+  int key[NF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    key[f] = j0 + 32 * (2 * wave + f) + (lane & 31);
+  for (int f = 0; f < NF; ++f) {
+    key[f] = j0 + 32 * (NF * wave + f) + (lane & 31);
     const bool ok = key[f] < n_c;
     const uint16_t* src =
         k_ctx + ((size_t)lh * n_c + (ok ? key[f] : 0)) * D + 8 * (lane >> 5);
@@ -102,21 +108,19 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     }
   };
 
-  float M[2] = {-__builtin_inff(), -__builtin_inff()};
-  auto reduce2 = [&](const f32x16& x0, const f32x16& x1) {
+  float M[NF];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      M[0] = max3f(M[0], x0[4 * u], max3f(x0[4 * u + 1], x0[4 * u + 2], x0[4 * u + 3]));
-      M[1] = max3f(M[1], x1[4 * u], max3f(x1[4 * u + 1], x1[4 * u + 2], x1[4 * u + 3]));
-    }
+  for (int f = 0; f < NF; ++f) M[f] = -__builtin_inff();
+  auto reduceN = [&](const f32x16* x) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        M[f] = max3f(M[f], x[f][4 * u], max3f(x[f][4 * u + 1], x[f][4 * u + 2], x[f][4 * u + 3]));
   };
 
-  f32x16 p0, p1;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
-
   // one 32-row subtile: seed with -lse/scale of the lane's 16 rows (-inf
-  // for rows past R), run the products, reduce the previous subtile
+  // for rows past R), run the products, fold them into the running maxima
   auto subtile = [&](const uint16_t* sb, const float* slb, bool partial, int rbase) {
     f32x16 init;
 #pragma unroll
@@ -131,16 +135,16 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
       for (int a = 0; a < 16; ++a)
         if ((8 * (a >> 2) + (a & 3)) > lim) init[a] = -__builtin_inff();
     }
-    f32x16 c0 = init, c1 = init;
+    f32x16 c[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) c[f] = init;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
-      c0 = mfma32(a, bk[0][s], c0);
-      c1 = mfma32(a, bk[1][s], c1);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], c[f]);
     }
-    reduce2(p0, p1);
-    p0 = c0;
-    p1 = c1;
+    reduceN(c);
   };
 
   auto step = [&](int t, auto buf_tag) {
@@ -169,10 +173,9 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
-  reduce2(p0, p1);
 
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const float mx = __builtin_fmaxf(M[f], __shfl_xor(M[f], 32));
     // the exact score is a probability, so never above 1
     const float sc = __builtin_fminf(fast_exp2(mx * c2), 1.0f);
@@ -184,7 +187,7 @@ template <int D>
 hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
                            const float* lse, float* scores, const ScoreShape& s,
                            hipStream_t stream) {
-  const int wg_per_head = (s.n_c + 255) / 256;
+  const int wg_per_head = (s.n_c + kKeysPerWg - 1) / kKeysPerWg;
   const long long grid = (long long)s.L * s.H * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
