@@ -35,12 +35,20 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 CALIB_BYTES = 1 << 30       # plain copy used to calibrate HBM byte counters
 
 
-def algorithmic_work(w, mode=0):
-    """Work the method itself requires (no padding, no masked tiles)."""
-    G, d, n_c, n_in = w.G, w.d, w.n_c, w.n_in
+def algorithmic_work(w, mode=0, chunk=None):
+    """Work the method itself requires (no padding, no masked tiles).  With
+    chunked scoring every chunk of m cached keys has n_prompt + m rows."""
+    G, d, n_c = w.G, w.d, w.n_c
     heads = w.L * w.H
-    logits1 = G * (n_in * n_c + n_in * (n_in + 1) // 2)   # every seen key, every row
-    logits2 = G * n_in * n_c                              # cached columns only
+    if chunk:
+        ms = [min(chunk, n_c - s) for s in range(0, n_c, min(chunk, n_c))]
+    else:
+        ms = [n_c]
+    logits1 = logits2 = 0
+    for m in ms:
+        n_in = w.n_prompt + m
+        logits1 += G * (n_in * m + n_in * (n_in + 1) // 2)   # every seen key, every row
+        logits2 += G * n_in * m                              # cached columns only
     total = synth_total(w, mode)
     return {
         "lse_flops": 2.0 * d * logits1 * heads,
@@ -85,7 +93,7 @@ def synth_total(w, mode):
     return w.L * kl
 
 
-def cpu_baseline(w, seconds: float, mode: int = 0):
+def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None):
     """The float64 oracle on whole heads of the workload, head after head,
     until `seconds` have passed (at least one head)."""
     import oracle
@@ -93,10 +101,14 @@ def cpu_baseline(w, seconds: float, mode: int = 0):
     done, t_oracle, heads = 0, 0.0, []
     order = [(l, h) for l in range(w.L) for h in range(w.H)]
     for (l, h) in order:
-        gen = synth.generate_head(w, l, h)
+        gen = synth.generate_chunked_head(w, l, h, chunk) if chunk else synth.generate_head(w, l, h)
         q, kc, kn = oracle.workload_head_inputs(gen)
         t0 = time.perf_counter()
-        S, _ = oracle.head_scores_parallel(q, kc, kn, float(w.scale), workers=workers)
+        if chunk:
+            S, _ = oracle.chunked_head_scores(q, kc, kn, float(w.scale), w.n_prompt, chunk,
+                                              w.G, workers=workers)
+        else:
+            S, _ = oracle.head_scores_parallel(q, kc, kn, float(w.scale), workers=workers)
         off, idx = oracle.select(S[None, None], w.keep_ratio, 0)
         oracle.compact(gen["k_ctx"][None, None], gen["v_ctx"][None, None], off, idx)
         t_oracle += time.perf_counter() - t0
@@ -123,6 +135,8 @@ def main():
     ap.add_argument("--workload", default=synth.LLAMA8B_8K.name,
                     choices=sorted(synth.BY_NAME))
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunked scoring with this chunk length (0 = whole context)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -135,16 +149,20 @@ def main():
         sys.exit(2)
 
     w = synth.BY_NAME[args.workload]
-    work = algorithmic_work(w, args.mode)
+    chunk = args.chunk or None
+    work = algorithmic_work(w, args.mode, chunk)
 
     # host work first: input generation and the oracle baseline (thread pools)
     t0 = time.perf_counter()
-    gen = synth.generate_workload(w, workers=min(16, synth.default_workers()))
+    if chunk:
+        gen = synth.generate_chunked_workload(w, chunk, workers=min(16, synth.default_workers()))
+    else:
+        gen = synth.generate_workload(w, workers=min(16, synth.default_workers()))
     t_gen = time.perf_counter() - t0
     print(f"# generated {w.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds, args.mode)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.mode, chunk)
         print(f"# cpu baseline: {cpu['value']:.3g} pairs/s", file=sys.stderr, flush=True)
 
     import torch
@@ -157,7 +175,11 @@ def main():
     L, H, G, n_c, n_in, d = w.L, w.H, w.G, w.n_c, w.n_in, w.d
     scale = float(w.scale)
     total = work["kept_rows"]
-    lse = torch.empty((L, H, G, n_in), dtype=torch.float32, device="cuda")
+    if chunk:
+        lse = torch.empty((L, H, synth.chunk_rows(w, chunk) * G), dtype=torch.float32,
+                          device="cuda")
+    else:
+        lse = torch.empty((L, H, G, n_in), dtype=torch.float32, device="cuda")
     scores = torch.empty((L, H, n_c), dtype=torch.float32, device="cuda")
     offsets = torch.empty(L * H + 1, dtype=torch.int64, device="cuda")
     idx = torch.empty(total, dtype=torch.int32, device="cuda")
@@ -172,9 +194,17 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        kvq.kvscore_lse(dev["q"], dev["k_ctx"], dev["k_new"], lse, scale, stream)
+        if chunk:
+            kvq.kvscore_chunked_lse(dev["q"], dev["k_ctx"], dev["k_new"], G, w.n_prompt,
+                                    chunk, lse, scale, stream)
+        else:
+            kvq.kvscore_lse(dev["q"], dev["k_ctx"], dev["k_new"], lse, scale, stream)
         mark(1)
-        kvq.kvscore_colmax(dev["q"], dev["k_ctx"], lse, scores, scale, stream)
+        if chunk:
+            kvq.kvscore_chunked_colmax(dev["q"], dev["k_ctx"], lse, G, w.n_prompt, chunk,
+                                       scores, scale, stream)
+        else:
+            kvq.kvscore_colmax(dev["q"], dev["k_ctx"], lse, scores, scale, stream)
         mark(2)
         kvq.kv_topk_select(scores, w.keep_ratio, args.mode, offsets, idx, stream)
         mark(3)
@@ -215,7 +245,7 @@ def main():
     sel_gbs = work["select_bytes"] / (ms["kv_topk_select"] * 1e-3) / 1e9
 
     dominant = max(names, key=lambda n: ms[n])
-    traffic = recorded_traffic(dominant, w.name)
+    traffic = recorded_traffic(dominant, w.name) if not chunk else None
     if dominant in ("kvscore_lse", "kvscore_colmax"):
         achieved = lse_tf if dominant == "kvscore_lse" else col_tf
         roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
@@ -242,7 +272,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "L": L, "H": H, "G": G, "d": d, "n_c": n_c,
                    "n_prompt": w.n_prompt, "keep_ratio": w.keep_ratio,
-                   "select_mode": args.mode},
+                   "select_mode": args.mode, "chunk": chunk},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v, 4) for n, v in ms.items()},

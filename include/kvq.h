@@ -102,6 +102,34 @@ int kvscore_colmax(const void* q, const void* k_ctx, const float* lse,
                    float* scores, int L, int H, int G, int d, int64_t n_c,
                    int64_t n_prompt, float scale, void* stream);
 
+/* Chunked scoring (KVzip section 3.4, chunk-based scoring): the context is
+ * split into chunks of `chunk` tokens (the last one shorter when chunk does
+ * not divide n_c); chunk c of every (l, h) is scored on its own, from a
+ * repeat pass over the prompt and that chunk only: m_c = min(chunk,
+ * n_c - c*chunk) cached keys [c*chunk, c*chunk + m_c) and n_in_c = n_prompt +
+ * m_c new keys, an n_in_c x (m_c + n_in_c) attention per query head, causal
+ * over the new keys, normalised over those keys only.  Each chunk's scores
+ * land at its keys' positions in the usual scores[l][h][n_c].
+ *
+ * Layouts (per (l, h), chunks packed back to back in chunk order):
+ *   q     bf16 [L][H][rows * G][d]   chunk c is a [G][n_in_c][d] block
+ *   k_new bf16 [L][H][rows][d]       chunk c is a [n_in_c][d] block
+ *   lse   fp32 [L][H][rows * G]      chunk c is a [G][n_in_c] block
+ *   k_ctx, scores as for the unchunked calls
+ * where rows = n_chunks * n_prompt + n_c (kv_chunk_layout).  chunk >= n_c is
+ * exactly the unchunked computation.  Same requirements and errors as the
+ * unchunked calls, plus chunk >= 1 and G * (n_prompt + min(chunk, n_c)) < 2^31. */
+int kv_chunk_layout(int64_t n_c, int64_t n_prompt, int64_t chunk,
+                    int64_t* n_chunks, int64_t* rows_per_head);
+int kvscore_chunked_lse(const void* q, const void* k_ctx, const void* k_new,
+                        float* lse, int L, int H, int G, int d, int64_t n_c,
+                        int64_t n_prompt, int64_t chunk, float scale,
+                        void* stream);
+int kvscore_chunked_colmax(const void* q, const void* k_ctx, const float* lse,
+                           float* scores, int L, int H, int G, int d,
+                           int64_t n_c, int64_t n_prompt, int64_t chunk,
+                           float scale, void* stream);
+
 /* Total kept count for kv_topk_select: L*H*k (mode 0, k = keep count of n_c)
  * or L*k_L (mode 1, k_L = keep count of H*n_c).  Pure host function. */
 int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,

@@ -19,6 +19,9 @@ Cache Compression with Context Reconstruction"):
   n_c cached-key columns is A-bar; the score of cached key j is the maximum of
   A-bar[g, i, j] over all g and all n_in rows i (the displayed equation of
   that section).
+* Section 3.4 (chunk-based scoring): each chunk of m context tokens is
+  scored from its own repeat pass (prompt + that chunk), on an
+  n_in x (m + n_in) attention over the chunk's cached keys and new keys.
 * Section 4.1 (eviction structure): keep the r% highest-scoring KV pairs.
 
 Readings taken where the page is silent (each one is listed with its reason in
@@ -153,6 +156,55 @@ def head_scores_parallel(q, k_ctx, k_new, scale, workers: int,
         for smax in ex.map(block, jobs):
             np.maximum(S, smax, out=S)
     return S, lse
+
+
+# ----------------------------------------------------------------------------
+# KVzip section 3.4: chunked scoring
+# ----------------------------------------------------------------------------
+def chunk_bounds(n_c: int, chunk: int):
+    """(first key, length) of every chunk: fixed length `chunk`, the last one
+    shorter when chunk does not divide n_c."""
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    return [(s, min(chunk, n_c - s)) for s in range(0, n_c, chunk)]
+
+
+def chunked_head_scores(q_packed: np.ndarray, k_ctx: np.ndarray,
+                        k_new_packed: np.ndarray, scale: float, n_prompt: int,
+                        chunk: int, G: int, workers: int = 1
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+    """Chunk-based scoring of one (layer, KV head).
+
+    Each chunk of m_c context tokens is reconstructed on its own: the repeat
+    prompt followed by the chunk gives n_in_c = n_prompt + m_c queries per
+    query head and n_in_c new keys, and the chunk's m_c cached keys plus those
+    new keys form an n_in_c x (m_c + n_in_c) attention; the chunk's keys are
+    scored from it exactly as in section 3.2.
+
+    q_packed     : (rows * G, d) - chunk blocks [G][n_in_c][d] back to back
+    k_new_packed : (rows, d)     - chunk blocks [n_in_c][d] back to back
+    returns (S (n_c,), lse_packed (rows * G,))
+    """
+    n_c, d = k_ctx.shape
+    S = np.zeros(n_c)
+    lse_parts = []
+    qo = ko = 0
+    for start, m in chunk_bounds(n_c, chunk):
+        n_in = n_prompt + m
+        qc = q_packed[qo:qo + G * n_in].reshape(G, n_in, d)
+        kn = k_new_packed[ko:ko + n_in]
+        kc = k_ctx[start:start + m]
+        if workers > 1:
+            Sc, lc = head_scores_parallel(qc, kc, kn, scale, workers=workers)
+        else:
+            Sc, lc = head_scores(qc, kc, kn, scale)
+        S[start:start + m] = Sc
+        lse_parts.append(lc.reshape(-1))
+        qo += G * n_in
+        ko += n_in
+    if qo != q_packed.shape[0] or ko != k_new_packed.shape[0]:
+        raise ValueError("packed chunk layout does not match n_c, n_prompt, chunk")
+    return S, np.concatenate(lse_parts)
 
 
 # ----------------------------------------------------------------------------

@@ -17,7 +17,8 @@ KV_ERR_HIP = -5
 # every symbol declared in include/kvq.h
 EXPORTS = (
     "kv_status_string", "kv_last_hip_error", "kv_keep_count", "kvscore_lse",
-    "kvscore_colmax", "kv_topk_total", "kv_topk_workspace_bytes",
+    "kvscore_colmax", "kv_chunk_layout", "kvscore_chunked_lse",
+    "kvscore_chunked_colmax", "kv_topk_total", "kv_topk_workspace_bytes",
     "kv_topk_select", "kv_compact",
 )
 
@@ -58,6 +59,9 @@ def load() -> ctypes.CDLL:
         "kv_keep_count": (i32, [i64, f64, ctypes.POINTER(i64)]),
         "kvscore_lse": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, f32, vp]),
         "kvscore_colmax": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, f32, vp]),
+        "kv_chunk_layout": (i32, [i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "kvscore_chunked_lse": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i64, f32, vp]),
+        "kvscore_chunked_colmax": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i64, f32, vp]),
         "kv_topk_total": (i32, [i32, i32, i64, f64, i32, ctypes.POINTER(i64)]),
         "kv_topk_workspace_bytes": (sz, [i32, i32, i64, i32]),
         "kv_topk_select": (i32, [vp, i32, i32, i64, f64, i32, vp, vp, i64, vp, sz, vp]),

@@ -133,6 +133,64 @@ def kvscore_colmax(q: torch.Tensor, k_ctx: torch.Tensor, lse: torch.Tensor,
     return scores
 
 
+def kv_chunk_layout(n_c: int, n_prompt: int, chunk: int) -> Tuple[int, int]:
+    """(n_chunks, rows per (l, h)) of the packed chunked layouts."""
+    nch, rows = ctypes.c_int64(), ctypes.c_int64()
+    _check("kv_chunk_layout", _lib.load().kv_chunk_layout(
+        n_c, n_prompt, chunk, ctypes.byref(nch), ctypes.byref(rows)))
+    return nch.value, rows.value
+
+
+def _chunked_dims(q, k_ctx, k_new, G, n_prompt, chunk):
+    if q.dim() != 4 or k_ctx.dim() != 4 or k_new.dim() != 4:
+        raise ValueError("q [L,H,rows*G,d], k_ctx [L,H,n_c,d], k_new [L,H,rows,d]")
+    L, H, n_c, d = k_ctx.shape
+    _, rows = kv_chunk_layout(n_c, n_prompt, chunk)
+    if tuple(q.shape) != (L, H, rows * G, d) or tuple(k_new.shape) != (L, H, rows, d):
+        raise ValueError("chunked q / k_new shapes disagree with the chunk layout")
+    return L, H, d, n_c, rows
+
+
+def kvscore_chunked_lse(q, k_ctx, k_new, G: int, n_prompt: int, chunk: int,
+                        lse=None, scale=None, stream=None):
+    """Pass 1 of chunked scoring (packed chunk layout, see kvq.h)."""
+    for t, n in ((q, "q"), (k_ctx, "k_ctx"), (k_new, "k_new")):
+        _dev(t, torch.bfloat16, n)
+    L, H, d, n_c, rows = _chunked_dims(q, k_ctx, k_new, G, n_prompt, chunk)
+    if lse is None:
+        lse = torch.empty((L, H, rows * G), dtype=torch.float32, device=q.device)
+    _dev(lse, torch.float32, "lse")
+    if tuple(lse.shape) != (L, H, rows * G):
+        raise ValueError("lse must be [L,H,rows*G]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("kvscore_chunked_lse", _lib.load().kvscore_chunked_lse(
+        _ptr(q), _ptr(k_ctx), _ptr(k_new), _ptr(lse), L, H, G, d, n_c, n_prompt,
+        chunk, float(scale), _stream(stream)))
+    return lse
+
+
+def kvscore_chunked_colmax(q, k_ctx, lse, G: int, n_prompt: int, chunk: int,
+                           scores=None, scale=None, stream=None):
+    """Pass 2 of chunked scoring; scores come out as [L,H,n_c]."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_ctx, torch.bfloat16, "k_ctx")
+    _dev(lse, torch.float32, "lse")
+    L, H, n_c, d = k_ctx.shape
+    _, rows = kv_chunk_layout(n_c, n_prompt, chunk)
+    if tuple(q.shape) != (L, H, rows * G, d) or tuple(lse.shape) != (L, H, rows * G):
+        raise ValueError("chunked q / lse shapes disagree with the chunk layout")
+    if scores is None:
+        scores = torch.empty((L, H, n_c), dtype=torch.float32, device=q.device)
+    _dev(scores, torch.float32, "scores")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("kvscore_chunked_colmax", _lib.load().kvscore_chunked_colmax(
+        _ptr(q), _ptr(k_ctx), _ptr(lse), _ptr(scores), L, H, G, d, n_c, n_prompt,
+        chunk, float(scale), _stream(stream)))
+    return scores
+
+
 def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
                    offsets: Optional[torch.Tensor] = None,
                    idx: Optional[torch.Tensor] = None,
@@ -195,6 +253,14 @@ def score(q, k_ctx, k_new, scale=None, stream=None):
     """(scores, lse) of every cached key: pass 1 then pass 2."""
     lse = kvscore_lse(q, k_ctx, k_new, scale=scale, stream=stream)
     scores = kvscore_colmax(q, k_ctx, lse, scale=scale, stream=stream)
+    return scores, lse
+
+
+def score_chunked(q, k_ctx, k_new, G, n_prompt, chunk, scale=None, stream=None):
+    """(scores, lse) of chunked scoring (KVzip section 3.4)."""
+    lse = kvscore_chunked_lse(q, k_ctx, k_new, G, n_prompt, chunk, scale=scale, stream=stream)
+    scores = kvscore_chunked_colmax(q, k_ctx, lse, G, n_prompt, chunk, scale=scale,
+                                    stream=stream)
     return scores, lse
 
 

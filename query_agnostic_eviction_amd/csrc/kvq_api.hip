@@ -41,13 +41,63 @@ int check_score_args(int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
   if (n_c >= (int64_t)1 << 31 || (int64_t)G * n_in >= (int64_t)1 << 31)
     return KV_ERR_INVALID_ARG;
   if ((int64_t)L * H >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
-  out->L = L;
-  out->H = H;
-  out->G = G;
-  out->d = d;
-  out->n_c = (int)n_c;
-  out->n_in = (int)n_in;
-  out->scale = scale;
+  *out = kvq::plain_shape(L, H, G, d, (int)n_c, (int)n_in, scale);
+  return KV_OK;
+}
+
+// Chunked scoring (KVzip page section 3.4): chunk c of each (l, h) covers
+// cached keys [c*chunk, c*chunk + m_c) with m_c = min(chunk, n_c - c*chunk)
+// and has its own n_prompt + m_c query positions; per (l, h) the chunks'
+// queries, new keys and lse are packed back to back (see kvq.h).  Full
+// chunks run as one launch with a work item per (l, h, chunk); a shorter
+// last chunk runs as a second launch with a work item per (l, h).
+struct ChunkPlan {
+  int n_launch;
+  kvq::ScoreShape s[2];
+};
+
+int plan_chunks(int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
+                int64_t chunk, float scale, ChunkPlan* plan) {
+  if (chunk < 1) return KV_ERR_INVALID_ARG;
+  kvq::ScoreShape base;
+  int st = check_score_args(L, H, G, d, n_c, n_prompt, scale, &base);
+  if (st != KV_OK) return st;
+  const int64_t m = chunk < n_c ? chunk : n_c;
+  const int64_t full = n_c / m, rem = n_c % m;
+  const int64_t nchunks = full + (rem ? 1 : 0);
+  const int64_t rows = nchunks * n_prompt + n_c;  // query positions per (l, h)
+  if ((int64_t)G * (n_prompt + m) >= ((int64_t)1 << 31) ||
+      (int64_t)L * H * full >= ((int64_t)1 << 31) || (int64_t)G * rows >= ((int64_t)1 << 40))
+    return KV_ERR_INVALID_ARG;
+  const long long dd = d, g = G;
+  const long long slot = n_prompt + m;           // positions of a full chunk
+  plan->n_launch = 0;
+  if (full > 0) {
+    kvq::ScoreShape& a = plan->s[plan->n_launch++];
+    a = base;
+    a.nheads = (int)((int64_t)L * H * full);
+    a.inner = (int)full;
+    a.n_c = (int)m;
+    a.n_in = (int)slot;
+    a.q = {0, g * rows * dd, g * slot * dd};
+    a.k_new = {0, rows * dd, slot * dd};
+    a.lse = {0, g * rows, g * slot};
+    a.k_ctx = {0, n_c * dd, m * dd};
+    a.scores = {0, n_c, m};
+  }
+  if (rem > 0) {
+    kvq::ScoreShape& b = plan->s[plan->n_launch++];
+    b = base;
+    b.nheads = L * H;
+    b.inner = 1;
+    b.n_c = (int)rem;
+    b.n_in = (int)(n_prompt + rem);
+    b.q = {full * g * slot * dd, g * rows * dd, 0};
+    b.k_new = {full * slot * dd, rows * dd, 0};
+    b.lse = {full * g * slot, g * rows, 0};
+    b.k_ctx = {full * m * dd, n_c * dd, 0};
+    b.scores = {full * m, n_c, 0};
+  }
   return KV_OK;
 }
 
@@ -104,6 +154,58 @@ int kvscore_colmax(const void* q, const void* k_ctx, const float* lse,
   return hip_status(kvq::launch_colmax(static_cast<const uint16_t*>(q),
                                        static_cast<const uint16_t*>(k_ctx), lse,
                                        scores, s, static_cast<hipStream_t>(stream)));
+}
+
+int kv_chunk_layout(int64_t n_c, int64_t n_prompt, int64_t chunk,
+                    int64_t* n_chunks, int64_t* rows_per_head) {
+  if (!n_chunks || !rows_per_head || n_c < 1 || n_prompt < 0 || chunk < 1)
+    return KV_ERR_INVALID_ARG;
+  const int64_t m = chunk < n_c ? chunk : n_c;
+  *n_chunks = (n_c + m - 1) / m;
+  *rows_per_head = *n_chunks * n_prompt + n_c;
+  return KV_OK;
+}
+
+int kvscore_chunked_lse(const void* q, const void* k_ctx, const void* k_new,
+                        float* lse, int L, int H, int G, int d, int64_t n_c,
+                        int64_t n_prompt, int64_t chunk, float scale,
+                        void* stream) {
+  if (!q || !k_ctx || !k_new || !lse) return KV_ERR_INVALID_ARG;
+  ChunkPlan plan;
+  int st = plan_chunks(L, H, G, d, n_c, n_prompt, chunk, scale, &plan);
+  if (st != KV_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_ctx, 16) || !aligned(k_new, 16) || !aligned(lse, 4))
+    return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  for (int i = 0; i < plan.n_launch; ++i) {
+    st = hip_status(kvq::launch_lse(static_cast<const uint16_t*>(q),
+                                    static_cast<const uint16_t*>(k_ctx),
+                                    static_cast<const uint16_t*>(k_new), lse,
+                                    plan.s[i], static_cast<hipStream_t>(stream)));
+    if (st != KV_OK) return st;
+  }
+  return KV_OK;
+}
+
+int kvscore_chunked_colmax(const void* q, const void* k_ctx, const float* lse,
+                           float* scores, int L, int H, int G, int d,
+                           int64_t n_c, int64_t n_prompt, int64_t chunk,
+                           float scale, void* stream) {
+  if (!q || !k_ctx || !lse || !scores) return KV_ERR_INVALID_ARG;
+  ChunkPlan plan;
+  int st = plan_chunks(L, H, G, d, n_c, n_prompt, chunk, scale, &plan);
+  if (st != KV_OK) return st;
+  if (!aligned(q, 16) || !aligned(k_ctx, 16) || !aligned(lse, 4) || !aligned(scores, 4))
+    return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  for (int i = 0; i < plan.n_launch; ++i) {
+    st = hip_status(kvq::launch_colmax(static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k_ctx), lse,
+                                       scores, plan.s[i],
+                                       static_cast<hipStream_t>(stream)));
+    if (st != KV_OK) return st;
+  }
+  return KV_OK;
 }
 
 int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,

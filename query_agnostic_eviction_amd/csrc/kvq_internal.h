@@ -6,12 +6,45 @@
 
 namespace kvq {
 
-struct ScoreShape {
-  int L, H, G, d;
-  int n_c;        // cached keys per head
-  int n_in;       // query positions per head (n_prompt + n_c)
-  float scale;    // logit temperature
+// Where one tensor of work item ("head") u lives, as an element offset:
+//   off0 + (u / inner) * outer + (u % inner) * step
+// An unchunked call has one work item per (layer, KV head) and inner = 1;
+// chunked scoring has one per (layer, KV head, chunk) with inner = chunks.
+struct TensorMap {
+  long long off0, outer, step;
 };
+
+__host__ __device__ inline long long map_offset(const TensorMap& m, int u, int inner) {
+  return m.off0 + (long long)(u / inner) * m.outer + (long long)(u % inner) * m.step;
+}
+
+struct ScoreShape {
+  int nheads;     // work items of this launch
+  int inner;      // work items per (layer, KV head)
+  int G, d;
+  int n_c;        // cached keys per work item
+  int n_in;       // query positions per work item (n_prompt + its keys)
+  float scale;    // logit temperature
+  TensorMap q, k_new, lse, k_ctx, scores;
+};
+
+// The plain per-(layer, KV head) mapping of the layouts in kvq.h.
+inline ScoreShape plain_shape(int L, int H, int G, int d, int n_c, int n_in, float scale) {
+  ScoreShape s;
+  s.nheads = L * H;
+  s.inner = 1;
+  s.G = G;
+  s.d = d;
+  s.n_c = n_c;
+  s.n_in = n_in;
+  s.scale = scale;
+  s.q = {0, (long long)G * n_in * d, 0};
+  s.k_new = {0, (long long)n_in * d, 0};
+  s.lse = {0, (long long)G * n_in, 0};
+  s.k_ctx = {0, (long long)n_c * d, 0};
+  s.scores = {0, (long long)n_c, 0};
+  return s;
+}
 
 // Pass 1: row log-sum-exp over cached keys and causal new keys.
 hipError_t launch_lse(const uint16_t* q, const uint16_t* k_ctx,

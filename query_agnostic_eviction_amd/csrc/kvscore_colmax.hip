@@ -44,8 +44,9 @@ constexpr int kKeysPerWg = 4 * NF * 32;
 template <int D>
 __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
-    const float* __restrict__ lse, float* __restrict__ scores, int G, int n_c,
-    int n_in, int wg_per_head, float c2, float inv_scale) {
+    const float* __restrict__ lse, float* __restrict__ scores,
+    const ScoreShape sh, int wg_per_head, float c2, float inv_scale) {
+  const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
   using C = ColCfg<D>;
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[2 * TL::ELEMS];
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int lh = logical / wg_per_head;
+  const int u = logical / wg_per_head;  // work item: (layer, KV head[, chunk])
   const int j0 = (logical % wg_per_head) * kKeysPerWg;
 
   // this wave's two key fragments -> registers (B operand layout)
@@ -64,15 +65,16 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     key[f] = j0 + 32 * (NF * wave + f) + (lane & 31);
     const bool ok = key[f] < n_c;
     const uint16_t* src =
-        k_ctx + ((size_t)lh * n_c + (ok ? key[f] : 0)) * D + 8 * (lane >> 5);
+        k_ctx + map_offset(sh.k_ctx, u, sh.inner) + (size_t)(ok ? key[f] : 0) * D +
+        8 * (lane >> 5);
     const uint32_t keep = ok ? 0xffffffffu : 0u;  // keys past n_c read as zeros
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) bk[f][s] = as_bf16x8(ldg16(src + 16 * s) & keep);
   }
 
   const int R = G * n_in;  // flattened (g, i) rows of this head
-  const uint16_t* qh = q + (size_t)lh * R * D;
-  const float* lh_lse = lse + (size_t)lh * R;
+  const uint16_t* qh = q + map_offset(sh.q, u, sh.inner);
+  const float* lh_lse = lse + map_offset(sh.lse, u, sh.inner);
   const int T = (R + C::QT - 1) / C::QT;
 
   int src_rel[TL::LOADS];
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
     const float mx = __builtin_fmaxf(M[f], __shfl_xor(M[f], 32));
     // the exact score is a probability, so never above 1
     const float sc = __builtin_fminf(fast_exp2(mx * c2), 1.0f);
-    if (lane < 32 && key[f] < n_c) scores[(size_t)lh * n_c + key[f]] = sc;
+    if (lane < 32 && key[f] < n_c)
+      scores[map_offset(sh.scores, u, sh.inner) + key[f]] = sc;
   }
 }
 
@@ -188,13 +191,12 @@ hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
                            const float* lse, float* scores, const ScoreShape& s,
                            hipStream_t stream) {
   const int wg_per_head = (s.n_c + kKeysPerWg - 1) / kKeysPerWg;
-  const long long grid = (long long)s.L * s.H * wg_per_head;
+  const long long grid = (long long)s.nheads * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
   const float inv_scale = (float)(1.0 / (double)s.scale);
   hipLaunchKernelGGL(colmax_kernel<D>, dim3((unsigned)grid), dim3(256), 0,
-                     stream, q, k_ctx, lse, scores, s.G, s.n_c, s.n_in,
-                     wg_per_head, c2, inv_scale);
+                     stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
   return hipGetLastError();
 }
 

@@ -41,16 +41,17 @@ struct LseCfg {
 template <int D>
 __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
-    const uint16_t* __restrict__ k_new, float* __restrict__ lse, int G,
-    int n_c, int n_in, int nfrag_head, int wg_per_head, float c2,
-    float scale) {
+    const uint16_t* __restrict__ k_new, float* __restrict__ lse,
+    const ScoreShape sh, int nfrag_head, int wg_per_head, float c2) {
   using C = LseCfg<D>;
+  const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
+  const float scale = sh.scale;
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t sk[2 * TL::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int lh = logical / wg_per_head;
+  const int u = logical / wg_per_head;  // work item: (layer, KV head[, chunk])
   // latest positions (most keys) first
   const int wgi = wg_per_head - 1 - logical % wg_per_head;
 
@@ -76,16 +77,15 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
   for (int f = 0; f < 2; ++f) {
     const int pos = fpos0[f] + (lane & 31);
     const bool ok = fvalid[f] && pos < n_in;
-    const uint16_t* src =
-        q + ((size_t)((size_t)lh * G + fg[f]) * n_in + (ok ? pos : 0)) * D +
-        8 * (lane >> 5);
+    const uint16_t* src = q + map_offset(sh.q, u, sh.inner) +
+                          ((size_t)fg[f] * n_in + (ok ? pos : 0)) * D + 8 * (lane >> 5);
     const uint32_t keep = ok ? 0xffffffffu : 0u;  // padding rows read as zeros
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) bq[f][s] = as_bf16x8(ldg16(src + 16 * s) & keep);
   }
 
-  const uint16_t* seg_ptr[2] = {k_ctx + (size_t)lh * n_c * D,
-                                k_new + (size_t)lh * n_in * D};
+  const uint16_t* seg_ptr[2] = {k_ctx + map_offset(sh.k_ctx, u, sh.inner),
+                                k_new + map_offset(sh.k_new, u, sh.inner)};
   const int T0 = (n_c + C::KT - 1) / C::KT;
   const int T1 = (new_len + C::KT - 1) / C::KT;
   const int T = T0 + T1;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
     const float val = __builtin_fmaf(M, scale, __logf(S));
     const int pos = fpos0[f] + (lane & 31);
     if (lane < 32 && fvalid[f] && pos < n_in)
-      lse[((size_t)lh * G + fg[f]) * n_in + pos] = val;
+      lse[map_offset(sh.lse, u, sh.inner) + (size_t)fg[f] * n_in + pos] = val;
   }
 }
 
@@ -267,12 +267,11 @@ hipError_t launch_lse_d(const uint16_t* q, const uint16_t* k_ctx,
   const int nb = (s.n_in + 31) / 32;
   const int nfrag = s.G * nb;
   const int wg_per_head = (nfrag + 7) / 8;
-  const long long grid = (long long)s.L * s.H * wg_per_head;
+  const long long grid = (long long)s.nheads * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
   hipLaunchKernelGGL(lse_kernel<D>, dim3((unsigned)grid), dim3(256), 0, stream,
-                     q, k_ctx, k_new, lse, s.G, s.n_c, s.n_in, nfrag,
-                     wg_per_head, c2, s.scale);
+                     q, k_ctx, k_new, lse, s, nfrag, wg_per_head, c2);
   return hipGetLastError();
 }
 

@@ -5,5 +5,7 @@ selection or compaction arithmetic lives here.
 """
 from .configs import (ALL, BY_NAME, GEMMA12B_16K, LLAMA8B_128K, LLAMA8B_8K,
                       QWEN14B_32K, TINY, Workload)
-from .generate import (bf16_bits_to_f32, default_workers, f64_to_bf16_bits,
-                       generate_head, generate_workload)
+from .generate import (bf16_bits_to_f32, chunk_rows, default_workers,
+                       f64_to_bf16_bits, generate_chunked_head,
+                       generate_chunked_workload, generate_head,
+                       generate_workload)

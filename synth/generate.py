@@ -37,7 +37,8 @@ import numpy as np
 from . import configs as C
 from .configs import Workload
 
-STREAM_BASIS, STREAM_Q, STREAM_KCTX, STREAM_KNEW, STREAM_V, STREAM_STRUCT = range(6)
+(STREAM_BASIS, STREAM_Q, STREAM_KCTX, STREAM_KNEW, STREAM_V, STREAM_STRUCT,
+ STREAM_Q_CHUNKS, STREAM_KNEW_CHUNKS, STREAM_STRUCT_CHUNKS) = range(9)
 
 
 def _rng(w: Workload, l: int, h: int, stream: int) -> np.random.Generator:
@@ -146,6 +147,45 @@ def generate_head(w: Workload, l: int, h: int,
     return out
 
 
+def chunk_rows(w: Workload, chunk: int) -> int:
+    """Query positions per (l, h) over all chunks of the packed layout."""
+    n_chunks = -(-w.n_c // min(chunk, w.n_c))
+    return n_chunks * w.n_prompt + w.n_c
+
+
+def generate_chunked_head(w: Workload, l: int, h: int, chunk: int,
+                          parts: Iterable[str] = ("q", "k_ctx", "k_new", "v_ctx")
+                          ) -> Dict[str, np.ndarray]:
+    """Inputs of chunk-based scoring for one (l, h): every chunk has its own
+    repeat pass, so its queries and new keys are fresh draws of the same
+    recipe (streams 6 and 7; the Student-t key multipliers of the new keys
+    from stream 8).  The cached keys and values are those of generate_head.
+
+      q      uint16 [rows * G][d]   chunk blocks [G][n_prompt + m_c][d]
+      k_new  uint16 [rows][d]       chunk blocks [n_prompt + m_c][d]
+      k_ctx, v_ctx as generate_head
+    """
+    parts = tuple(parts)
+    out = generate_head(w, l, h, [p for p in parts if p in ("k_ctx", "v_ctx")])
+    basis = _basis(w, l, h)
+    m = min(chunk, w.n_c)
+    bounds = [(s0, min(m, w.n_c - s0)) for s0 in range(0, w.n_c, m)]
+    if "q" in parts:
+        rng = _rng(w, l, h, STREAM_Q_CHUNKS)
+        blocks = [_rows(rng, w.G * (w.n_prompt + mc), w, basis) for _, mc in bounds]
+        out["q"] = f64_to_bf16_bits(np.concatenate(blocks))
+    if "k_new" in parts:
+        rng = _rng(w, l, h, STREAM_KNEW_CHUNKS)
+        blocks = [_rows(rng, w.n_prompt + mc, w, basis) for _, mc in bounds]
+        kn = np.concatenate(blocks)
+        if w.structure == "student_t":
+            t = np.abs(_rng(w, l, h, STREAM_STRUCT_CHUNKS).standard_t(C.STUDENT_T_NU,
+                                                                       size=kn.shape[0]))
+            kn *= t[:, None]
+        out["k_new"] = f64_to_bf16_bits(kn)
+    return out
+
+
 def _head_job(args):
     w, l, h, parts = args
     return l, h, generate_head(w, l, h, parts)
@@ -195,4 +235,33 @@ def generate_workload(w: Workload,
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1), ThreadPoolExecutor(min(workers, len(jobs))) as ex:
             list(ex.map(run, jobs))
+    return out
+
+
+def generate_chunked_workload(w: Workload, chunk: int,
+                              workers: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """generate_chunked_head for every (l, h), as [L][H]-indexed arrays:
+    q [L][H][rows*G][d], k_new [L][H][rows][d], k_ctx / v_ctx [L][H][n_c][d]."""
+    rows = chunk_rows(w, chunk)
+    out = {"q": np.zeros((w.L, w.H, rows * w.G, w.d), np.uint16),
+           "k_new": np.zeros((w.L, w.H, rows, w.d), np.uint16),
+           "k_ctx": np.zeros((w.L, w.H, w.n_c, w.d), np.uint16),
+           "v_ctx": np.zeros((w.L, w.H, w.n_c, w.d), np.uint16)}
+
+    def run(lh):
+        l, h = lh
+        g = generate_chunked_head(w, l, h, chunk)
+        for p in out:
+            out[p][l, h] = g[p]
+
+    heads = [(l, h) for l in range(w.L) for h in range(w.H)]
+    workers = default_workers() if workers is None else workers
+    if workers <= 1:
+        for lh in heads:
+            run(lh)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+            list(ex.map(run, heads))
     return out

@@ -167,3 +167,31 @@ def test_binding_rejects_host_tensors():
         kvq.kvscore_lse(q, k, k)
     with pytest.raises(ValueError):
         kvq.kv_topk_select(torch.zeros((1, 1, 4)), 0.5)
+
+
+def test_chunk_layout(lib):
+    nch, rows = ctypes.c_int64(), ctypes.c_int64()
+    for n_c, n_p, chunk, want in [(131072, 32, 2048, (64, 64 * 32 + 131072)),
+                                  (1000, 3, 300, (4, 12 + 1000)), (7, 0, 10, (1, 7)),
+                                  (5, 2, 1, (5, 15))]:
+        assert lib.kv_chunk_layout(n_c, n_p, chunk, ctypes.byref(nch), ctypes.byref(rows)) == OK
+        assert (nch.value, rows.value) == want
+    assert lib.kv_chunk_layout(0, 1, 1, ctypes.byref(nch), ctypes.byref(rows)) == INV
+    assert lib.kv_chunk_layout(5, 1, 0, ctypes.byref(nch), ctypes.byref(rows)) == INV
+
+
+@pytest.mark.parametrize("name", ["kvscore_chunked_lse", "kvscore_chunked_colmax"])
+def test_chunked_validation(lib, name):
+    fn = getattr(lib, name)
+
+    def call(q=P, a=P, b=P, c=P, L=1, H=1, G=4, d=128, n_c=64, n_p=2, chunk=16, scale=0.1):
+        return fn(q, a, b, c, L, H, G, d, n_c, n_p, chunk, scale, NUL)
+    assert call(chunk=0) == INV
+    assert call(chunk=-5) == INV
+    assert call(q=NUL) == INV
+    assert call(c=NUL) == INV
+    assert call(d=96) == UNS
+    assert call(G=9) == UNS
+    assert call(n_c=0) == INV
+    assert call(scale=math.nan) == INV
+    assert call(q=P2) == ALN

@@ -402,3 +402,93 @@ def test_llama8b_128k_full_size_sampled():
     eq = np.flatnonzero(s32 == thr)
     kept_eq = np.intersect1d(kept, eq)
     assert np.array_equal(kept_eq, eq[:kept_eq.size]), "ties must go to the lower index"
+
+
+# ---------------------------------------------------------------------------
+# chunked scoring (KVzip page, section 3.4)
+# ---------------------------------------------------------------------------
+def _chunked_inputs(w, chunk, heads=None):
+    rows = synth.chunk_rows(w, chunk)
+    gens = {}
+    q = np.zeros((w.L, w.H, rows * w.G, w.d), np.uint16)
+    kn = np.zeros((w.L, w.H, rows, w.d), np.uint16)
+    kc = np.zeros((w.L, w.H, w.n_c, w.d), np.uint16)
+    for l in range(w.L):
+        for h in range(w.H):
+            if heads is not None and (l, h) not in heads:
+                continue
+            g = synth.generate_chunked_head(w, l, h, chunk, ("q", "k_ctx", "k_new"))
+            gens[(l, h)] = g
+            q[l, h], kn[l, h], kc[l, h] = g["q"], g["k_new"], g["k_ctx"]
+    return gens, {"q": to_dev_bf16(q), "k_new": to_dev_bf16(kn), "k_ctx": to_dev_bf16(kc)}
+
+
+CHUNKED = [
+    # (base, G, d, n_c, n_prompt, chunk, L, H)
+    ("tiny", 4, 64, 512, 16, 128, 1, 1),
+    ("tiny", 4, 64, 512, 16, 200, 1, 2),
+    ("llama3.1-8b-8k", 4, 128, 1000, 32, 300, 2, 1),
+    ("gemma3-12b-16k", 2, 256, 300, 5, 64, 1, 2),
+    ("qwen2.5-14b-32k", 5, 128, 77, 0, 1, 1, 1),
+    ("llama3.1-8b-8k", 3, 128, 70, 3, 1000, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[f"d{c[2]}-nc{c[3]}-m{c[5]}" for c in CHUNKED])
+def test_chunked_parity(case):
+    base, G, d, n_c, n_p, chunk, L, H = case
+    w = synth.BY_NAME[base].shrink(G=G, d=d, n_c=n_c, n_prompt=n_p, L=L, H=H,
+                                   rank=min(synth.BY_NAME[base].rank, d))
+    _say("case:", case)
+    gens, dev = _chunked_inputs(w, chunk)
+    sc, lse = kvq.score_chunked(dev["q"], dev["k_ctx"], dev["k_new"], G, n_p, chunk,
+                                scale=float(w.scale))
+    torch.cuda.synchronize()
+    for (l, h), g in gens.items():
+        S, l_ref = oracle.chunked_head_scores(
+            oracle.bf16_to_f64(g["q"]), oracle.bf16_to_f64(g["k_ctx"]),
+            oracle.bf16_to_f64(g["k_new"]), float(w.scale), n_p, chunk, G)
+        check_lse(lse[l, h].cpu().numpy(), l_ref, f"lse[{l},{h}]")
+        check_scores(sc[l, h].cpu().numpy(), S, f"scores[{l},{h}]")
+
+
+def test_chunked_whole_context_equals_unchunked():
+    w = synth.LLAMA8B_8K.shrink(n_c=777, n_prompt=9, L=1, H=2)
+    gen = synth.generate_workload(w, workers=1)
+    dev = _upload(gen)
+    sc0 = kvq.kvscore_colmax(dev["q"], dev["k_ctx"],
+                             kvq.kvscore_lse(dev["q"], dev["k_ctx"], dev["k_new"], scale=float(w.scale)),
+                             scale=float(w.scale))
+    q = dev["q"].reshape(w.L, w.H, w.G * w.n_in, w.d)
+    for chunk in (w.n_c, 5000):
+        sc1, _ = kvq.score_chunked(q, dev["k_ctx"], dev["k_new"], w.G, w.n_prompt, chunk,
+                                   scale=float(w.scale))
+        assert torch.equal(sc0, sc1)
+
+
+def test_llama8b_128k_chunked_full_size():
+    w = synth.LLAMA8B_128K
+    chunk = 2048
+    heads = [(0, 0), (31, 7)]
+    _say("case: chunked full", w.name, chunk)
+    rows = synth.chunk_rows(w, chunk)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    q = torch.randn((w.L, w.H, rows * w.G, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((w.L, w.H, rows, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.randn((w.L, w.H, w.n_c, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    gens = {}
+    for (l, h) in heads:
+        gh = synth.generate_chunked_head(w, l, h, chunk, ("q", "k_ctx", "k_new"))
+        gens[(l, h)] = gh
+        q[l, h], kn[l, h], kc[l, h] = to_dev_bf16(gh["q"]), to_dev_bf16(gh["k_new"]), to_dev_bf16(gh["k_ctx"])
+    sc, lse = kvq.score_chunked(q, kc, kn, w.G, w.n_prompt, chunk, scale=float(w.scale))
+    torch.cuda.synchronize()
+    for (l, h) in heads:
+        gh = gens[(l, h)]
+        S, l_ref = oracle.chunked_head_scores(
+            oracle.bf16_to_f64(gh["q"]), oracle.bf16_to_f64(gh["k_ctx"]),
+            oracle.bf16_to_f64(gh["k_new"]), float(w.scale), w.n_prompt, chunk, w.G,
+            workers=WORKERS)
+        check_lse(lse[l, h].cpu().numpy(), l_ref, f"lse[{l},{h}]")
+        check_scores(sc[l, h].cpu().numpy(), S, f"scores[{l},{h}]")

@@ -333,3 +333,80 @@ def test_planted_mask_mistakes_are_caught(monkeypatch, mutant):
     except (AssertionError, ValueError, IndexError):
         caught += 1
     assert caught == 2
+
+
+# ---------------------------------------------------------------------------
+# chunked scoring (KVzip page, section 3.4)
+# ---------------------------------------------------------------------------
+def _pack_chunks(rng, G, n_c, n_prompt, d, chunk, amp=1.0):
+    k_ctx = amp * rng.standard_normal((n_c, d))
+    qs, kns = [], []
+    for _, m in OK.chunk_bounds(n_c, chunk):
+        qs.append(amp * rng.standard_normal((G * (n_prompt + m), d)))
+        kns.append(amp * rng.standard_normal((n_prompt + m, d)))
+    return np.concatenate(qs), k_ctx, np.concatenate(kns)
+
+
+def test_chunk_bounds():
+    assert OK.chunk_bounds(10, 4) == [(0, 4), (4, 4), (8, 2)]
+    assert OK.chunk_bounds(8, 4) == [(0, 4), (4, 4)]
+    assert OK.chunk_bounds(3, 10) == [(0, 3)]
+    assert OK.chunk_bounds(5, 1) == [(j, 1) for j in range(5)]
+
+
+def test_chunked_whole_context_is_unchunked():
+    rng = np.random.default_rng(20)
+    G, n_c, n_p, d = 3, 40, 4, 8
+    q, kc, kn = _rand_head(rng, G, n_c, n_p, d)
+    S, lse = oracle.head_scores(q, kc, kn, 0.3)
+    for chunk in (n_c, n_c + 1, 10 ** 6):
+        S2, l2 = oracle.chunked_head_scores(q.reshape(-1, d), kc, kn, 0.3, n_p, chunk, G)
+        np.testing.assert_array_equal(S2, S)
+        np.testing.assert_array_equal(l2, lse.reshape(-1))
+
+
+def test_chunked_zero_queries_closed_form():
+    rng = np.random.default_rng(21)
+    G, n_c, n_p, d, chunk = 2, 23, 3, 5, 7
+    q, kc, kn = _pack_chunks(rng, G, n_c, n_p, d, chunk, amp=2.0)
+    q[:] = 0.0
+    S, lse = oracle.chunked_head_scores(q, kc, kn, 0.5, n_p, chunk, G)
+    off = 0
+    for start, m in OK.chunk_bounds(n_c, chunk):
+        # each chunk is its own uniform attention over m + i + 1 keys
+        np.testing.assert_allclose(S[start:start + m], 1.0 / (m + 1), rtol=1e-14)
+        want = np.tile(np.log(m + np.arange(n_p + m) + 1.0), G)
+        np.testing.assert_allclose(lse[off:off + G * (n_p + m)], want, atol=1e-13)
+        off += G * (n_p + m)
+
+
+def test_chunked_single_key_chunks_are_logistic():
+    # chunk = 1, n_prompt = 0: chunk j holds cached key j and one new key,
+    # so S_j = max_g logistic(scale * q_gj . (k_ctx[j] - k_new[j]))
+    rng = np.random.default_rng(22)
+    G, n_c, d, scale = 3, 9, 4, 0.7
+    q, kc, kn = _pack_chunks(rng, G, n_c, 0, d, 1, amp=1.5)
+    S, _ = oracle.chunked_head_scores(q, kc, kn, scale, 0, 1, G)
+    for j in range(n_c):
+        qj = q[G * j:G * (j + 1)]
+        want = scipy.special.expit(scale * qj @ (kc[j] - kn[j])).max()
+        assert S[j] == pytest.approx(want, rel=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunked_brute_force(seed):
+    rng = np.random.default_rng(400 + seed)
+    G, n_c, n_p, d = 1 + seed % 3, 5 + seed, seed % 3, 1 + seed % 3
+    chunk = 1 + seed % 4
+    q, kc, kn = _pack_chunks(rng, G, n_c, n_p, d, chunk)
+    S, lse = oracle.chunked_head_scores(q, kc, kn, 0.6, n_p, chunk, G)
+    qo = ko = 0
+    for start, m in OK.chunk_bounds(n_c, chunk):
+        n_in = n_p + m
+        qc = q[qo:qo + G * n_in].reshape(G, n_in, d)
+        Sb, lb, _ = brute_scores(qc.tolist(), kc[start:start + m].tolist(),
+                                 kn[ko:ko + n_in].tolist(), 0.6)
+        np.testing.assert_allclose(S[start:start + m], Sb, rtol=1e-12)
+        np.testing.assert_allclose(lse[qo:qo + G * n_in], np.ravel(lb), rtol=1e-12, atol=1e-12)
+        qo += G * n_in
+        ko += n_in
