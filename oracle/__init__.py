@@ -6,6 +6,6 @@ oracle.kvzip for the definitions it follows and oracle.brute for the scalar
 brute force that pins it.
 """
 from .kvzip import (attention_rows, bf16_to_f64, chunk_bounds,
-                    chunked_head_scores, compact, head_scores,
-                    head_scores_parallel, keep_count, row_lse, select,
+                    chunked_head_scores, compact, head_level_scores,
+                    head_scores, head_scores_parallel, keep_count, row_lse, select,
                     topk_ascending, visible_keys, workload_head_inputs)

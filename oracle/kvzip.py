@@ -233,6 +233,10 @@ def select(scores: np.ndarray, keep_ratio: float, mode: int
     mode 0 : per (l, h), k = keep_count(n_c, r) in every head
     mode 1 : per layer, one top-k_L over the H * n_c flattened scores,
              k_L = keep_count(H * n_c, r); heads end up with different counts
+    mode 2 : one top-k over all L * H * n_c scores of the model (the budget
+             shared across every head of every layer), k = keep_count(L * H *
+             n_c, r); equal scores go to the lower flattened index
+             (l * H + h) * n_c + j
     returns offsets int64 (L*H + 1,), idx int32 (total,) - idx holds positions
     j in [0, n_c), ascending within each (l, h), heads in (l, h) order.
     """
@@ -250,13 +254,30 @@ def select(scores: np.ndarray, keep_ratio: float, mode: int
             for h in range(H):
                 sel = flat[(flat >= h * n_c) & (flat < (h + 1) * n_c)]
                 per_head.append(sel - h * n_c)
+    elif mode == 2:
+        flat = topk_ascending(scores.reshape(-1), keep_count(L * H * n_c, keep_ratio))
+        for lh in range(L * H):
+            sel = flat[(flat >= lh * n_c) & (flat < (lh + 1) * n_c)]
+            per_head.append(sel - lh * n_c)
     else:
-        raise ValueError("mode must be 0 or 1")
+        raise ValueError("mode must be 0, 1 or 2")
     counts = np.array([len(x) for x in per_head], dtype=np.int64)
     offsets = np.zeros(L * H + 1, dtype=np.int64)
     np.cumsum(counts, out=offsets[1:])
     idx = (np.concatenate(per_head) if per_head else np.zeros(0)).astype(np.int32)
     return offsets, idx
+
+
+# ----------------------------------------------------------------------------
+# KVzip section 4.2: head-level (context-independent) score
+# ----------------------------------------------------------------------------
+def head_level_scores(scores: np.ndarray) -> np.ndarray:
+    """One static score per (l, h): the largest pair score of the head along
+    the sequence.  scores: (L, H, n_c) -> (L, H)."""
+    scores = np.asarray(scores)
+    if scores.ndim != 3 or scores.shape[2] < 1:
+        raise ValueError("scores must be (L, H, n_c) with n_c >= 1")
+    return scores.max(axis=2)
 
 
 # ----------------------------------------------------------------------------

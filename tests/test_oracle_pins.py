@@ -286,13 +286,70 @@ def test_layer_budget_brute(seed):
     assert off[-1] == L * kl
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_model_budget_brute(seed):
+    # mode 2: one budget over every head of every layer (KVzip section 4.1)
+    rng = np.random.default_rng(400 + seed)
+    L, H, n_c = 2, 2, 4
+    s = rng.integers(0, 3, size=(L, H, n_c)).astype(np.float64) / 2.0
+    r = [0.25, 0.34, 0.5, 0.67, 0.1, 0.9][seed]
+    off, idx = oracle.select(s, r, 2)
+    k = oracle.keep_count(L * H * n_c, r)
+    want = brute_topk(list(s.reshape(-1)), k)
+    got = []
+    for lh in range(L * H):
+        got += [lh * n_c + j for j in idx[off[lh]:off[lh + 1]]]
+    assert got == want
+    assert off[-1] == k and off[0] == 0
+
+
+def test_model_budget_reduces_to_other_modes():
+    rng = np.random.default_rng(13)
+    s = rng.random((1, 3, 40))
+    for r in (0.05, 0.3, 0.77, 1.0):
+        a, b = oracle.select(s, r, 2), oracle.select(s, r, 1)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    s = rng.random((1, 1, 40))
+    for r in (0.05, 0.3, 1.0):
+        a, b = oracle.select(s, r, 2), oracle.select(s, r, 0)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # a head whose scores all exceed another's takes its whole share first
+    s = np.stack([rng.random(30) + 2.0, rng.random(30)])[None]
+    off, idx = oracle.select(s, 0.5, 2)
+    assert off.tolist() == [0, 30, 30] and idx.tolist() == list(range(30))
+
+
+def test_head_level_scores():
+    # KVzip section 4.2: the head score is the max along the sequence
+    with pytest.raises(ValueError):
+        oracle.head_level_scores(np.zeros((2, 2, 0)))
+    # zero queries: every row is uniform, row 0 sees n_c + 1 keys, so the
+    # head score is 1 / (n_c + 1)
+    for n_c, n_p in [(1, 0), (5, 3), (17, 2)]:
+        q = np.zeros((2, n_p + n_c, 4))
+        S, _ = oracle.head_scores(q, np.ones((n_c, 4)), np.ones((n_p + n_c, 4)), 0.5)
+        hs = oracle.head_level_scores(S[None, None])
+        assert hs.shape == (1, 1) and abs(hs[0, 0] - 1.0 / (n_c + 1)) < 1e-15
+    # brute force: the largest attention weight any cached key gets anywhere
+    rng = np.random.default_rng(14)
+    for _ in range(5):
+        G, n_c, n_p, d = 2, 5, 2, 3
+        q = rng.normal(size=(G, n_p + n_c, d))
+        kc, kn = rng.normal(size=(n_c, d)), rng.normal(size=(n_p + n_c, d))
+        _, _, A = brute_scores(q.tolist(), kc.tolist(), kn.tolist(), 0.7)
+        want = max(A[g][i][j] for g in range(G) for i in range(n_p + n_c)
+                   for j in range(n_c))
+        S, _ = oracle.head_scores(q, kc, kn, 0.7)
+        assert abs(oracle.head_level_scores(S[None, None])[0, 0] - want) < 1e-13
+
+
 def test_compact_rows_are_kept_rows():
     rng = np.random.default_rng(12)
     L, H, n_c, d = 2, 2, 20, 4
     k = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
     v = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
     s = rng.random((L, H, n_c))
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         off, idx = oracle.select(s, 0.35, mode)
         ko, vo = oracle.compact(k, v, off, idx)
         assert ko.shape == (off[-1], d)
