@@ -54,8 +54,10 @@ def algorithmic_work(w, mode=0, chunk=None):
         "lse_flops": 2.0 * d * logits1 * heads,
         "lse_exps": float(logits1 * heads),
         "colmax_flops": 2.0 * d * logits2 * heads,
-        # scores read 3 histogram passes + 1 ordered pass; idx + offsets written
-        "select_bytes": 4.0 * 4 * heads * n_c + 4.0 * total + 8.0 * (heads + 1),
+        # scores read by 3 histogram passes and 1 ordered pass (mode 2 adds a
+        # counting pass); idx + offsets written
+        "select_bytes": 4.0 * (5 if mode == 2 else 4) * heads * n_c + 4.0 * total
+                        + 8.0 * (heads + 1),
         # K and V rows read and written, plus the index of each row
         "compact_bytes": 2.0 * 2 * 2 * d * total + 4.0 * total,
         "kept_rows": total,
@@ -89,6 +91,9 @@ def synth_total(w, mode):
     if mode == 0:
         k = min(max(math.floor(w.keep_ratio * w.n_c), 1), w.n_c)
         return w.L * w.H * k
+    if mode == 2:
+        n = w.L * w.H * w.n_c
+        return min(max(math.floor(w.keep_ratio * n), 1), n)
     kl = min(max(math.floor(w.keep_ratio * w.H * w.n_c), 1), w.H * w.n_c)
     return w.L * kl
 
@@ -134,7 +139,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=synth.LLAMA8B_8K.name,
                     choices=sorted(synth.BY_NAME))
-    ap.add_argument("--mode", type=int, default=0, choices=(0, 1))
+    ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked scoring with this chunk length (0 = whole context)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -185,6 +190,8 @@ def main():
     idx = torch.empty(total, dtype=torch.int32, device="cuda")
     k_out = torch.empty((total, d), dtype=torch.bfloat16, device="cuda")
     v_out = torch.empty((total, d), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = kvq.kv_topk_workspace_bytes(w.L, w.H, w.n_c, args.mode)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     names = ("kvscore_lse", "kvscore_colmax", "kv_topk_select", "kv_compact")
@@ -206,7 +213,7 @@ def main():
         else:
             kvq.kvscore_colmax(dev["q"], dev["k_ctx"], lse, scores, scale, stream)
         mark(2)
-        kvq.kv_topk_select(scores, w.keep_ratio, args.mode, offsets, idx, stream)
+        kvq.kv_topk_select(scores, w.keep_ratio, args.mode, offsets, idx, stream, ws)
         mark(3)
         kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, k_out, v_out, stream)
         mark(4)

@@ -64,7 +64,7 @@ extern "C" {
 /* status codes */
 #define KV_OK                0
 #define KV_ERR_INVALID_ARG  -1  /* null pointer, non-positive size, ratio out of (0,1], size overflow */
-#define KV_ERR_UNSUPPORTED  -2  /* d not in {64, 128, 256}, G not in [1, 8], mode not in {0, 1} */
+#define KV_ERR_UNSUPPORTED  -2  /* d not in {64, 128, 256}, G not in [1, 8], mode not in {0, 1, 2} */
 #define KV_ERR_ALIGNMENT    -3  /* a pointer breaks the alignment rule above */
 #define KV_ERR_CAPACITY     -4  /* idx capacity or workspace too small */
 #define KV_ERR_HIP          -5  /* a HIP runtime call or launch failed */
@@ -130,21 +130,29 @@ int kvscore_chunked_colmax(const void* q, const void* k_ctx, const float* lse,
                            int64_t n_c, int64_t n_prompt, int64_t chunk,
                            float scale, void* stream);
 
-/* Total kept count for kv_topk_select: L*H*k (mode 0, k = keep count of n_c)
- * or L*k_L (mode 1, k_L = keep count of H*n_c).  Pure host function. */
+/* Total kept count for kv_topk_select: L*H*k (mode 0, k = keep count of n_c),
+ * L*k_L (mode 1, k_L = keep count of H*n_c) or k_M (mode 2, keep count of
+ * L*H*n_c).  Pure host function. */
 int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
                   int64_t* total_out);
 
-/* Scratch bytes kv_topk_select needs for these sizes (currently 0 for every
- * shape; NULL workspace is accepted when the size is 0). */
+/* Device scratch bytes kv_topk_select needs for these sizes: 0 for modes 0
+ * and 1 (NULL workspace accepted), about 16 KiB + 16 B per 4096 scores for
+ * mode 2.  The workspace is owned by the caller, must be 256-byte aligned,
+ * need not be initialised, and must not be shared by overlapping calls. */
 size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode);
 
 /* Selection (KVzip section 4.1): keeps the highest scores.
  *   mode 0: per (l, h), the k = clamp(floor(r * n_c), 1, n_c) largest;
  *   mode 1: per layer l, the k_L = clamp(floor(r * H * n_c), 1, H * n_c)
  *           largest of the layer's H * n_c scores (a non-uniform per-head
- *           budget); heads receive different counts.
- * Equal scores go to the lower index (j, or h * n_c + j in mode 1).  Writes
+ *           budget); heads receive different counts;
+ *   mode 2: the k_M = clamp(floor(r * L * H * n_c), 1, L * H * n_c) largest
+ *           of all the model's scores (one budget across every head of every
+ *           layer); layers and heads receive different counts.
+ * Equal scores go to the lower index (j; h * n_c + j in mode 1; (l * H + h) *
+ * n_c + j in mode 2).  Mode 2 runs as a sequence of grid-wide launches and
+ * needs the workspace of kv_topk_workspace_bytes.  Writes
  * offsets[L*H + 1] (offsets[l*H + h] = first kept row of that head) and the
  * kept positions j into idx, ascending within each head.  scores must be
  * non-negative (they are ordered by their IEEE bit pattern).  capacity is the
@@ -153,6 +161,14 @@ int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
                    double keep_ratio, int mode, int64_t* offsets, int32_t* idx,
                    int64_t capacity, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* Head-level static score (KVzip section 4.2, context-independent
+ * eviction): head_scores[l][h] = max_j scores[l][h][j], the largest pair
+ * score of each head along the sequence, as fp32 [L][H].  Exact (a max of
+ * the inputs, no rounding).  The heads can then be ranked by running
+ * kv_topk_select on head_scores viewed as [1][1][L*H]. */
+int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
+                   float* head_scores, void* stream);
 
 /* Compaction (KVzip section 2.1, KV_p as a subset of KV_c): for every head
  * (l, h) and every t in [offsets[l*H+h], offsets[l*H+h+1]) copies

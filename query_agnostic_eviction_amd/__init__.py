@@ -7,7 +7,7 @@ compaction, as hand-written gfx950 HIP kernels in libkvq.so behind a C ABI
 fails loudly when the library has not been built.
 """
 from .api import (KvqError, evict, kv_chunk_layout, kv_compact, kv_keep_count,
-                  kv_status_string, kv_topk_select, kv_topk_total,
+                  kv_head_scores, kv_status_string, kv_topk_select, kv_topk_total,
                   kv_topk_workspace_bytes, kvscore_chunked_colmax,
                   kvscore_chunked_lse, kvscore_colmax, kvscore_lse, score,
                   score_chunked)

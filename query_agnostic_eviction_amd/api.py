@@ -194,8 +194,10 @@ def kvscore_chunked_colmax(q, k_ctx, lse, G: int, n_prompt: int, chunk: int,
 def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
                    offsets: Optional[torch.Tensor] = None,
                    idx: Optional[torch.Tensor] = None,
-                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Kept positions per head (mode 0) or per layer (mode 1), CSR form."""
+                   stream=None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Kept positions, CSR form: budget per head (mode 0), per layer (mode 1)
+    or over the whole model (mode 2)."""
     _dev(scores, torch.float32, "scores")
     if scores.dim() != 3:
         raise ValueError("scores must be [L,H,n_c]")
@@ -210,11 +212,34 @@ def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
     ws_bytes = kv_topk_workspace_bytes(L, H, n_c, mode)
     ws = None
     if ws_bytes:
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+        if workspace is not None:
+            _dev(workspace, torch.uint8, "workspace")
+            if workspace.numel() < ws_bytes:
+                raise ValueError("workspace too small")
+            ws = workspace
+        else:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
     _check("kv_topk_select", _lib.load().kv_topk_select(
         _ptr(scores), L, H, n_c, float(keep_ratio), mode, _ptr(offsets), _ptr(idx),
         idx.numel(), _ptr(ws), ws_bytes, _stream(stream)))
     return offsets, idx
+
+
+def kv_head_scores(scores: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Head-level static score (KVzip section 4.2): max of each head's scores."""
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 3:
+        raise ValueError("scores must be [L,H,n_c]")
+    L, H, n_c = scores.shape
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32, device=scores.device)
+    _dev(out, torch.float32, "out")
+    if out.numel() != L * H:
+        raise ValueError("out must hold L*H entries")
+    _check("kv_head_scores", _lib.load().kv_head_scores(
+        _ptr(scores), L, H, n_c, _ptr(out), _stream(stream)))
+    return out
 
 
 def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,

@@ -212,39 +212,57 @@ int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
                   int64_t* total_out) {
   if (!total_out || L < 1 || H < 1 || n_c < 1 || !valid_ratio(keep_ratio))
     return KV_ERR_INVALID_ARG;
-  if (mode != 0 && mode != 1) return KV_ERR_UNSUPPORTED;
+  if (mode < 0 || mode > 2) return KV_ERR_UNSUPPORTED;
   if ((int64_t)H * n_c >= (int64_t)1 << 31 || (int64_t)L * H >= (int64_t)1 << 31)
     return KV_ERR_INVALID_ARG;
   if (mode == 0)
     *total_out = (int64_t)L * H * keep_count_of(n_c, keep_ratio);
-  else
+  else if (mode == 1)
     *total_out = (int64_t)L * keep_count_of((int64_t)H * n_c, keep_ratio);
+  else
+    *total_out = keep_count_of((int64_t)L * H * n_c, keep_ratio);
   return KV_OK;
 }
 
 size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode) {
-  (void)L; (void)H; (void)n_c; (void)mode;
-  return 0;
+  if (mode != 2 || L < 1 || H < 1 || n_c < 1) return 0;
+  return kvq::global_select_workspace((int64_t)L * H * n_c);
 }
 
 int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
                    double keep_ratio, int mode, int64_t* offsets, int32_t* idx,
                    int64_t capacity, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  (void)workspace;
   if (!scores || !offsets || !idx) return KV_ERR_INVALID_ARG;
   int64_t total = 0;
   int st = kv_topk_total(L, H, n_c, keep_ratio, mode, &total);
   if (st != KV_OK) return st;
   if (!aligned(scores, 4) || !aligned(offsets, 8) || !aligned(idx, 4))
     return KV_ERR_ALIGNMENT;
-  if (capacity < total || workspace_bytes < kv_topk_workspace_bytes(L, H, n_c, mode))
-    return KV_ERR_CAPACITY;
+  const size_t ws_need = kv_topk_workspace_bytes(L, H, n_c, mode);
+  if (capacity < total || workspace_bytes < ws_need) return KV_ERR_CAPACITY;
+  if (ws_need && !workspace) return KV_ERR_INVALID_ARG;
+  if (ws_need && !aligned(workspace, 256)) return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  if (mode == 2)
+    return hip_status(kvq::launch_global_topk(scores, (int64_t)L * H * n_c, (int)n_c, L * H,
+                                              total, offsets, idx, workspace,
+                                              static_cast<hipStream_t>(stream)));
   const int64_t k = mode == 0 ? keep_count_of(n_c, keep_ratio)
                               : keep_count_of((int64_t)H * n_c, keep_ratio);
-  (void)hipGetLastError();
   return hip_status(kvq::launch_topk(scores, L, H, (int)n_c, mode, k, offsets,
                                      idx, static_cast<hipStream_t>(stream)));
+}
+
+int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
+                   float* head_scores, void* stream) {
+  if (!scores || !head_scores || L < 1 || H < 1 || n_c < 1) return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31 || (int64_t)H * n_c >= (int64_t)1 << 31)
+    return KV_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || !aligned(head_scores, 4)) return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_head_max(scores, L * H, (int)n_c, head_scores,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,

@@ -61,6 +61,17 @@ hipError_t launch_topk(const float* scores, int L, int H, int n_c, int mode,
                        int64_t k_per_segment, int64_t* offsets, int32_t* idx,
                        hipStream_t stream);
 
+// Model-wide top-k over n scores (heads of n_c each) through the workspace.
+long long global_select_per_block(long long n);
+size_t global_select_workspace(long long n);
+hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nheads,
+                              long long k, int64_t* offsets, int32_t* idx,
+                              void* workspace, hipStream_t stream);
+
+// Max of each head's scores.
+hipError_t launch_head_max(const float* scores, int nheads, int n_c, float* out,
+                           hipStream_t stream);
+
 // Gather of kept rows; see kv_compact.
 hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
                           const int64_t* offsets, const int32_t* idx,

@@ -80,6 +80,30 @@ def check_topk_band(kept: np.ndarray, ref_scores: np.ndarray, k: int) -> int:
     return int(np.sum((ref_scores >= lo) & (ref_scores <= hi)))
 
 
+def check_valid_topk(scores: np.ndarray, kept: np.ndarray, k: int) -> None:
+    """A kept set of flat positions is a valid top-k of these very scores,
+    ties to the lower position (a property check that needs no oracle):
+    k distinct ascending positions, no dropped score above the smallest kept
+    one, and the kept scores equal to it are the lowest such positions."""
+    scores = np.asarray(scores).reshape(-1)
+    kept = np.asarray(kept, dtype=np.int64)
+    assert kept.size == k and np.all(np.diff(kept) > 0), "k ascending positions"
+    mask = np.zeros(scores.size, dtype=bool)
+    mask[kept] = True
+    thr = scores[mask].min()
+    assert not np.any(scores[~mask] > thr), "a dropped score outranks a kept one"
+    eq = np.flatnonzero(scores == thr)
+    n_kept_eq = int(np.count_nonzero(mask[eq]))
+    assert np.all(mask[eq[:n_kept_eq]]), "ties must go to the lower position"
+
+
+def flat_kept(offsets: np.ndarray, idx: np.ndarray, n_c: int) -> np.ndarray:
+    """Flat positions (l*H + h)*n_c + j of a CSR kept set."""
+    counts = np.diff(offsets)
+    heads = np.repeat(np.arange(counts.size, dtype=np.int64), counts)
+    return heads * n_c + idx[:offsets[-1]].astype(np.int64)
+
+
 def oracle_head(gen: dict, scale: float, workers: int = 1):
     q, kc, kn = oracle.workload_head_inputs(gen)
     if workers > 1:

@@ -78,9 +78,15 @@ def test_topk_total(lib):
     assert out.value == 256 * 2457
     assert lib.kv_topk_total(48, 8, 16384, 0.1, 1, ctypes.byref(out)) == OK
     assert out.value == 48 * 13107
-    assert lib.kv_topk_total(48, 8, 16384, 0.1, 2, ctypes.byref(out)) == UNS
+    assert lib.kv_topk_total(48, 8, 16384, 0.1, 2, ctypes.byref(out)) == OK
+    assert out.value == oracle.keep_count(48 * 8 * 16384, 0.1)
+    assert lib.kv_topk_total(48, 8, 16384, 0.1, 3, ctypes.byref(out)) == UNS
     assert lib.kv_topk_total(0, 8, 16384, 0.1, 0, ctypes.byref(out)) == INV
     assert lib.kv_topk_workspace_bytes(32, 8, 8192, 0) == 0
+    assert lib.kv_topk_workspace_bytes(32, 8, 8192, 1) == 0
+    ws = lib.kv_topk_workspace_bytes(32, 8, 8192, 2)
+    assert 16384 <= ws <= 16384 + 16 * 1024 + 1024
+    assert lib.kv_topk_workspace_bytes(1, 1, 1, 2) >= 16384
 
 
 def _lse(lib, q=P, kc=P, kn=P, lse=P, L=1, H=1, G=4, d=128, n_c=16, n_p=2, scale=0.1):
@@ -132,13 +138,28 @@ def test_select_validation(lib):
     assert _sel(lib, idx=NUL) == INV
     for r in (0.0, 1.01, -0.2, math.nan):
         assert _sel(lib, r=r) == INV
-    assert _sel(lib, mode=2) == UNS
+    assert _sel(lib, mode=3) == UNS
     assert _sel(lib, mode=-1) == UNS
+    wsb = lib.kv_topk_workspace_bytes(2, 2, 100, 2)
+    assert _sel(lib, mode=2, cap=119) == CAP
+    assert _sel(lib, mode=2, wsb=wsb - 1, ws=P) == CAP
+    assert _sel(lib, mode=2, wsb=wsb, ws=NUL) == INV
+    assert _sel(lib, mode=2, wsb=wsb, ws=ctypes.c_void_p(0x10080)) == ALN
     assert _sel(lib, n_c=0) == INV
     assert _sel(lib, cap=4 * 30 - 1) == CAP
     assert _sel(lib, mode=1, cap=2 * 60 - 1) == CAP
     assert _sel(lib, off=P4) == ALN
     assert _sel(lib, sc=P2) == ALN
+
+
+def test_head_scores_validation(lib):
+    f = lib.kv_head_scores
+    assert f(NUL, 2, 2, 10, P, NUL) == INV
+    assert f(P, 2, 2, 10, NUL, NUL) == INV
+    assert f(P, 0, 2, 10, P, NUL) == INV
+    assert f(P, 2, 2, 0, P, NUL) == INV
+    assert f(P2, 2, 2, 10, P, NUL) == ALN
+    assert f(P, 2, 2, 10, P2, NUL) == ALN
 
 
 def _cmp(lib, kc=P, vc=P, off=P, idx=P, ko=P, vo=P, L=2, H=2, d=128, n_c=100, total=120):

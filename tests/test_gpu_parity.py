@@ -12,8 +12,8 @@ import torch
 import oracle
 import synth
 import query_agnostic_eviction_amd as kvq
-from parity_util import (check_lse, check_scores, check_topk_band, dev_bf16_bits,
-                         head_kept, oracle_head, to_dev_bf16)
+from parity_util import (check_lse, check_scores, check_topk_band, check_valid_topk,
+                         dev_bf16_bits, flat_kept, head_kept, oracle_head, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,7 @@ def test_ragged_shapes(case):
                                    rank=min(synth.BY_NAME[base].rank, d))
     _say("case:", case)
     gen = synth.generate_workload(w, workers=1)
-    for mode in w.modes if len(w.modes) > 1 else (0, 1):
+    for mode in (0, 1, 2):
         out = _run(w, _upload(gen), mode)
         S_ref = _full_check(w, gen, out)
         _select_checks(w, gen, out, S_ref, [(l, h) for l in range(L) for h in range(H)], mode)
@@ -143,7 +143,7 @@ def test_zero_queries_closed_form():
 def test_keep_all_is_identity():
     w = synth.TINY.shrink(keep_ratio=1.0, L=2, H=2, n_c=300)
     gen = synth.generate_workload(w, workers=1)
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         out = _run(w, _upload(gen), mode)
         assert np.array_equal(out["idx"].cpu().numpy(), np.tile(np.arange(300), 4))
         assert np.array_equal(out["offsets"].cpu().numpy(), np.arange(5) * 300)
@@ -158,7 +158,7 @@ def test_select_ties_bit_exact(n_c, L, H):
     s = (rng.integers(0, 6, size=(L, H, n_c)).astype(np.float32) / 8.0)
     s[0, 0, :min(n_c, 3)] = 0.0
     dev = torch.from_numpy(s).cuda()
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         for r in (0.01, 0.1, 0.3, 0.5, 0.77, 1.0):
             o, i = kvq.kv_topk_select(dev, r, mode)
             ro, ri = oracle.select(s, r, mode)
@@ -173,12 +173,54 @@ def test_select_distinct_bit_patterns():
     s[1, 1, 100:200] = 0.0
     s[2, 0, 5] = 1.0
     dev = torch.from_numpy(s).cuda()
-    for mode in (0, 1):
+    for mode in (0, 1, 2):
         for r in (0.001, 0.25, 0.9):
             o, i = kvq.kv_topk_select(dev, r, mode)
             ro, ri = oracle.select(s, r, mode)
             assert np.array_equal(o.cpu().numpy(), ro)
             assert np.array_equal(i.cpu().numpy(), ri)
+
+
+# model-wide budget (mode 2) at the full score-array sizes of the workloads
+MODEL_BUDGET = [(32, 8, 8192, 0.3), (48, 8, 16384, 0.1), (32, 8, 131072, 0.3),
+                (3, 5, 2999, 0.5), (1, 1, 4097, 0.001)]
+
+
+@pytest.mark.parametrize("L,H,n_c,r", MODEL_BUDGET,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in MODEL_BUDGET])
+def test_model_budget_bit_exact(L, H, n_c, r):
+    _say("case: model budget", L, H, n_c, r)
+    rng = np.random.default_rng(L * H + n_c)
+    # quantised scores: long runs of exact ties across blocks and heads, with
+    # per-head offsets so that heads get very different counts
+    s = rng.integers(0, 64, size=(L, H, n_c)).astype(np.float32) / 256.0
+    s += (rng.integers(0, 4, size=(L, H, 1)) / 16.0).astype(np.float32)
+    dev = torch.from_numpy(s).cuda()
+    ws = torch.empty(kvq.kv_topk_workspace_bytes(L, H, n_c, 2), dtype=torch.uint8,
+                     device="cuda")
+    for rr in (r, 1.0):
+        o, i = kvq.kv_topk_select(dev, rr, 2, workspace=ws)
+        ro, ri = oracle.select(s, rr, 2)
+        assert np.array_equal(o.cpu().numpy(), ro), rr
+        assert np.array_equal(i.cpu().numpy(), ri), rr
+    # head-level scores and a ranking of the heads by them
+    hs = kvq.kv_head_scores(dev)
+    ref = oracle.head_level_scores(s)
+    assert np.array_equal(hs.cpu().numpy(), ref)
+    o, i = kvq.kv_topk_select(hs.reshape(1, 1, L * H), 0.5, 0)
+    ro, ri = oracle.select(ref.reshape(1, 1, L * H), 0.5, 0)
+    assert np.array_equal(i.cpu().numpy(), ri)
+
+
+def test_head_scores_shapes():
+    rng = np.random.default_rng(21)
+    for (L, H, n_c) in [(1, 1, 1), (2, 3, 5), (5, 1, 1000), (1, 7, 64), (2, 2, 131073)]:
+        s = rng.random((L, H, n_c)).astype(np.float32)
+        s[0, 0, -1] = 1.0
+        if n_c > 1:
+            s[-1, -1, :] = 0.0
+        got = kvq.kv_head_scores(torch.from_numpy(s).cuda()).cpu().numpy()
+        assert np.array_equal(got, oracle.head_level_scores(s)), (L, H, n_c)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -360,6 +402,34 @@ def test_gemma12b_16k_full_size_both_modes():
     o2, i2 = kvq.kv_topk_select(torch.from_numpy(s32).cuda(), w.keep_ratio, 1)
     ro, ri = oracle.select(s32, w.keep_ratio, 1)
     assert np.array_equal(o2.cpu().numpy(), ro) and np.array_equal(i2.cpu().numpy(), ri)
+    # mode 2 (one budget over the model) on the GPU scores: a valid top-k of
+    # those scores, and compaction of it equal to the kept input rows
+    _model_budget_checks(w, dev, sc, heads, S_ref)
+
+
+def _model_budget_checks(w, dev, sc, heads, S_ref):
+    off2, idx2 = kvq.kv_topk_select(sc, w.keep_ratio, 2)
+    ko, vo = kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], off2, idx2)
+    off2 = off2.cpu().numpy()
+    idx2 = idx2.cpu().numpy()
+    km = oracle.keep_count(w.L * w.H * w.n_c, w.keep_ratio)
+    assert off2[0] == 0 and off2[-1] == km and np.all(np.diff(off2) >= 0)
+    sc_np = sc.cpu().numpy()
+    check_valid_topk(sc_np, flat_kept(off2, idx2, w.n_c), km)
+    _say(f"model budget: {km} kept, per-head counts "
+         f"{np.diff(off2).min()}..{np.diff(off2).max()}")
+    hs = kvq.kv_head_scores(sc).cpu().numpy()
+    assert np.array_equal(hs, sc_np.max(axis=2))
+    for (l, h) in heads:
+        lh = l * w.H + h
+        rows = idx2[off2[lh]:off2[lh + 1]]
+        assert np.array_equal(dev_bf16_bits(ko[off2[lh]:off2[lh + 1]]),
+                              dev_bf16_bits(dev["k_ctx"][l, h])[rows])
+        assert np.array_equal(dev_bf16_bits(vo[off2[lh]:off2[lh + 1]]),
+                              dev_bf16_bits(dev["v_ctx"][l, h])[rows])
+        if S_ref is not None:   # head-level score against the oracle's
+            check_scores(hs[l, h:h + 1], np.array([S_ref[(l, h)].max()]),
+                         f"head score ({l},{h})")
 
 
 def test_llama8b_128k_full_size_sampled():
@@ -402,6 +472,8 @@ def test_llama8b_128k_full_size_sampled():
     eq = np.flatnonzero(s32 == thr)
     kept_eq = np.intersect1d(kept, eq)
     assert np.array_equal(kept_eq, eq[:kept_eq.size]), "ties must go to the lower index"
+    # one budget over the whole model's 33.5M scores
+    _model_budget_checks(w, dev, out["scores"], [(l, h)], None)
 
 
 # ---------------------------------------------------------------------------
