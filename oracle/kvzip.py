@@ -37,8 +37,11 @@ the project's design notes):
     floor rule m = floor(rho * n) of the SelKV page, section 3.1);
   - ties go to the lower index (the flattened h * n_c + j across heads), and
     kept indices are returned in ascending position order;
-  - the "across all heads" budget of section 4.1 is read per layer (mode 1);
-    mode 0 keeps the same count in every (layer, KV head).
+  - the "across all heads" budget of section 4.1 is read per layer (mode 1)
+    and over the whole model (mode 2); mode 0 keeps the same count in every
+    (layer, KV head);
+  - section 4.2's head-level score of a head is the largest of its pair
+    scores along the sequence.
 """
 from __future__ import annotations
 
