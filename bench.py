@@ -86,6 +86,22 @@ def recorded_traffic(kernel: str, workload: str):
     return None
 
 
+def calibration_copy(torch):
+    """A plain 1 GiB device-to-device copy, run once untimed and once timed:
+    its bytes read + written per second are the practical HBM ceiling of a
+    streaming kernel on this part, and under rocprofv3 --pmc its FETCH_SIZE /
+    WRITE_SIZE calibrate the counters."""
+    src = torch.empty(CALIB_BYTES // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * CALIB_BYTES / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def synth_total(w, mode):
     import math
     if mode == 0:
@@ -138,7 +154,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=synth.LLAMA8B_8K.name,
-                    choices=sorted(synth.BY_NAME))
+                    choices=sorted(synth.BY_NAME) + sorted(synth.EPI_BY_NAME))
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked scoring with this chunk length (0 = whole context)")
@@ -153,6 +169,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in synth.EPI_BY_NAME:
+        return run_epikv(args)
     w = synth.BY_NAME[args.workload]
     chunk = args.chunk or None
     work = algorithmic_work(w, args.mode, chunk)
@@ -237,10 +255,7 @@ def main():
 
     # a plain device copy of known size after the timed region: under
     # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the counters
-    calib_src = torch.empty(CALIB_BYTES // 2, dtype=torch.int16, device="cuda")
-    torch.empty_like(calib_src).copy_(calib_src)
-    torch.cuda.synchronize()
-    del calib_src
+    copy_gbs = calibration_copy(torch)
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = w.context_pairs / (elapsed / args.steps)
@@ -288,6 +303,160 @@ def main():
         "colmax_mfma_frac": round(col_tf / PEAK_BF16_TFLOPS, 4),
         "compact_hbm_frac": round(cmp_gbs / PEAK_HBM_GBS, 4),
         "select_gbs": round(sel_gbs, 1),
+        "copy_gbs": round(copy_gbs, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# attention-free EpiKV path (EpiKV page, section 3.2): hidden-state deltas,
+# band scores, top-K tokens, token compaction of every (layer, head)
+# ---------------------------------------------------------------------------
+def epikv_work(w):
+    nl = len(w.layers)
+    kept = w.L * w.H * w.budget
+    return {
+        # each hidden row read once, g written
+        "deltas_bytes": 2.0 * nl * w.n * w.D + 4.0 * nl * w.n,
+        "scores_bytes": 4.0 * nl * w.n + 4.0 * w.n,
+        # scores read by 3 histogram passes, a counting pass and the write
+        "select_bytes": 4.0 * 5 * w.n + 4.0 * w.budget,
+        # K and V rows read and written
+        "compact_bytes": 2.0 * 2 * 2 * w.d * kept + 4.0 * w.budget,
+    }
+
+
+def epikv_cpu_baseline(w, hidden, seconds):
+    """The float64 oracle on a prefix of the trace (the first N tokens, N
+    doubled until a run takes half the budget or covers the trace)."""
+    import oracle
+    from oracle import epikv as E
+    from threadpoolctl import threadpool_limits
+    rng = np.random.default_rng(0)
+    na = len(w.band_a)
+    N = min(4096, w.n)
+    while True:
+        k = max(1, w.budget * N // w.n)
+        kc = rng.integers(0, 2 ** 16, size=(w.L, w.H, N, w.d), dtype=np.uint16)
+        vc = rng.integers(0, 2 ** 16, size=(w.L, w.H, N, w.d), dtype=np.uint16)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            g = [E.hidden_deltas(oracle.bf16_to_f64(hidden[l, :N]))
+                 for l in range(hidden.shape[0])]
+            sc = E.token_scores(g[:na], g[na:], w.window, w.eps, True)
+            idx = E.select_tokens(sc, k)
+            E.compact_tokens(kc, vc, idx)
+            t = time.perf_counter() - t0
+        del kc, vc
+        if t >= seconds / 2 or N >= w.n:
+            break
+        N = min(w.n, 2 * N)
+    return {
+        "value": w.L * w.H * N / t,
+        "unit": "KV pairs/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {N} of {w.n} tokens of {w.name}: float64 deltas of "
+                  f"{hidden.shape[0]} hidden layers, rolling z-scores, top-{k}, gather of "
+                  f"{w.L}x{w.H} heads; {t:.1f} s",
+    }
+
+
+def run_epikv(args):
+    w = synth.EPI_BY_NAME[args.workload]
+    work = epikv_work(w)
+    t0 = time.perf_counter()
+    hidden = synth.generate_hidden(w, workers=min(16, synth.default_workers()))
+    print(f"# generated {w.name} hidden states in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = epikv_cpu_baseline(w, hidden, args.cpu_seconds)
+        print(f"# cpu baseline: {cpu['value']:.3g} pairs/s", file=sys.stderr, flush=True)
+
+    import torch
+    import query_agnostic_eviction_amd as kvq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    h = torch.from_numpy(hidden.view(np.int16)).view(torch.bfloat16).cuda()
+    del hidden
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    shape = (w.L, w.H, w.n, w.d)
+    kc = torch.randint(-32768, 32767, shape, dtype=torch.int16, device="cuda",
+                       generator=gen).view(torch.bfloat16)
+    vc = torch.randint(-32768, 32767, shape, dtype=torch.int16, device="cuda",
+                       generator=gen).view(torch.bfloat16)
+    nl, na = len(w.layers), len(w.band_a)
+    g = torch.empty((nl, w.n), dtype=torch.float32, device="cuda")
+    scores = torch.empty(w.n, dtype=torch.float32, device="cuda")
+    idx = torch.empty(w.budget, dtype=torch.int32, device="cuda")
+    k_out = torch.empty((w.L, w.H, w.budget, w.d), dtype=torch.bfloat16, device="cuda")
+    v_out = torch.empty_like(k_out)
+    sel_ws = torch.empty(kvq.kv_select_tokens_workspace_bytes(w.n), dtype=torch.uint8,
+                         device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ("kv_epi_deltas", "kv_epi_scores", "kv_select_tokens", "kv_compact_tokens")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        kvq.kv_epi_deltas(h, g, stream)
+        mark(1)
+        kvq.kv_epi_scores(g, na, w.window, w.eps, True, scores, stream)
+        mark(2)
+        kvq.kv_select_tokens(scores, w.budget, idx, stream, sel_ws)
+        mark(3)
+        kvq.kv_compact_tokens(kc, vc, idx, k_out, v_out, stream)
+        mark(4)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"# warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                            for s in range(args.steps)]))
+          for i, n in enumerate(names)}
+    copy_gbs = calibration_copy(torch)
+
+    key = {"kv_epi_deltas": "deltas_bytes", "kv_epi_scores": "scores_bytes",
+           "kv_select_tokens": "select_bytes", "kv_compact_tokens": "compact_bytes"}
+    gbs = {n: work[key[n]] / (ms[n] * 1e-3) / 1e9 for n in names}
+    dominant = max(names, key=lambda n: ms[n])
+    roof = {"kernel": dominant, "bound": "hbm", "achieved": round(gbs[dominant], 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs[dominant] / PEAK_HBM_GBS, 4),
+            "traffic": recorded_traffic(dominant, w.name)}
+    line = {
+        "metric": "context KV pairs scored+compacted/sec",
+        "value": w.kv_pairs / (elapsed / args.steps),
+        "unit": "KV pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "L": w.L, "H": w.H, "d": w.d, "D": w.D, "n": w.n,
+                   "budget": w.budget, "band_a": list(w.band_a), "band_b": list(w.band_b),
+                   "window": w.window, "score": "EpiKV detrended (eq. 3)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_ms": {n: round(v, 4) for n, v in ms.items()},
+        "hbm_frac": {n: round(gbs[n] / PEAK_HBM_GBS, 4) for n in names},
+        "copy_gbs": round(copy_gbs, 1),
     }
     print(json.dumps(line), flush=True)
 

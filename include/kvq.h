@@ -137,8 +137,8 @@ int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
                   int64_t* total_out);
 
 /* Device scratch bytes kv_topk_select needs for these sizes: 0 for modes 0
- * and 1 (NULL workspace accepted), about 16 KiB + 16 B per 4096 scores for
- * mode 2.  The workspace is owned by the caller, must be 256-byte aligned,
+ * and 1 (NULL workspace accepted), about 16 KiB + 16 B per 4096 scores (or
+ * per 1/1024 of the scores, whichever is more) for mode 2.  The workspace is owned by the caller, must be 256-byte aligned,
  * need not be initialised, and must not be shared by overlapping calls. */
 size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode);
 
@@ -180,6 +180,68 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention-free token score (page "EpiKV", section 3.2, equations 1-3) and
+ * token-level eviction under a budget of K tokens (section 3.1).  No
+ * attention matrix is involved: the score reads hidden states only.
+ *
+ * Readings fixed by this library where the page is silent:
+ *   - g(0) is undefined (no predecessor): stored as 0, in no window, and
+ *     position 0 scores 0;
+ *   - the window of position t >= 1 is the defined positions
+ *     max(1, t - w + 1) .. t, the current one included;
+ *   - sigma is the population standard deviation; eps is an argument;
+ *   - a band is a set of layers whose statistics are averaged (the page's
+ *     equations use one layer per band: 10 and 21);
+ *   - the same K positions are kept in every layer and KV head.
+ *
+ * Layouts:
+ *   h        bf16 [n_layers][n][D]     hidden states, band A's layers first
+ *   g        fp32 [n_layers][n]        hidden-state change norms
+ *   scores   fp32 [n]                  token scores (signed)
+ *   idx      int32 [K]                 kept positions, ascending
+ *   k_cache, v_cache bf16 [L][H][n][d]; k_out, v_out bf16 [L][H][K][d]
+ * ------------------------------------------------------------------------ */
+
+/* Equation 1: g[l][t] = || h[l][t] - h[l][t-1] ||_2 for t >= 1, g[l][0] = 0.
+ * Differences of the bf16 inputs are formed and squared in fp32 and summed
+ * in fp32 (relative error below 1e-5 for D <= 8192).  Requires n_layers,
+ * n >= 1 and D a multiple of 8 in [8, 8192] (else KV_ERR_UNSUPPORTED); h
+ * 16-byte aligned. */
+int kv_epi_deltas(const void* h, int n_layers, int64_t n, int D, float* g,
+                  void* stream);
+
+/* Equations 2 and 3: for t >= 1, with W(t) the window above,
+ *   detrend = 1:  stat_l(t) = (g_l(t) - mean_W g_l) / (std_W g_l + eps)
+ *   detrend = 0:  stat_l(t) = mean_W g_l
+ *   scores[t] = mean over band A (rows 0..n_a-1 of g) of stat_l(t)
+ *             - mean over band B (rows n_a..n_a+n_b-1) of stat_l(t),
+ * scores[0] = 0.  Window statistics in fp64, result rounded to fp32.
+ * Requires n_a, n_b >= 1, 1 <= window <= 1024 (above: KV_ERR_UNSUPPORTED),
+ * eps > 0 and finite, detrend in {0, 1}. */
+int kv_epi_scores(const float* g, int n_a, int n_b, int64_t n, int window,
+                  double eps, int detrend, float* scores, void* stream);
+
+/* Device scratch bytes kv_select_tokens needs for n scores (about 16 KiB
+ * plus 16 B per 4096 scores). */
+size_t kv_select_tokens_workspace_bytes(int64_t n);
+
+/* Budget of section 3.1: the k largest of n finite signed scores, ties (and
+ * -0.0 vs +0.0) to the lower position, written to idx[0..k) ascending.  Runs
+ * as a grid-wide radix select (six stream-ordered launches) in the caller's
+ * workspace: 256-byte aligned, uninitialised, at least
+ * kv_select_tokens_workspace_bytes(n) bytes (else KV_ERR_CAPACITY), not
+ * shared by overlapping calls.  Requires 1 <= k <= n < 2^31. */
+int kv_select_tokens(const float* scores, int64_t n, int64_t k, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Token-level compaction: k_out[l][h][t] = k_cache[l][h][idx[t]] and the
+ * same for v, bit for bit, for t < k, every (l, h).  An index outside
+ * [0, n) gives a zero row.  0 <= k <= n; d in {64, 128, 256}. */
+int kv_compact_tokens(const void* k_cache, const void* v_cache,
+                      const int32_t* idx, void* k_out, void* v_out, int L,
+                      int H, int d, int64_t n, int64_t k, void* stream);
 
 #ifdef __cplusplus
 }

@@ -272,6 +272,109 @@ def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
 
 
 # ---------------------------------------------------------------------------
+# attention-free token score (EpiKV page, section 3.2)
+# ---------------------------------------------------------------------------
+def kv_epi_deltas(h: torch.Tensor, g: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Eq. 1: g[l][t] = ||h[l][t] - h[l][t-1]||_2 (g[l][0] = 0); h bf16 [n_layers,n,D]."""
+    _dev(h, torch.bfloat16, "h")
+    if h.dim() != 3:
+        raise ValueError("h must be [n_layers, n, D]")
+    nl, n, D = h.shape
+    if g is None:
+        g = torch.empty((nl, n), dtype=torch.float32, device=h.device)
+    _dev(g, torch.float32, "g")
+    if g.numel() != nl * n:
+        raise ValueError("g must hold n_layers*n entries")
+    _check("kv_epi_deltas", _lib.load().kv_epi_deltas(_ptr(h), nl, n, D, _ptr(g),
+                                                      _stream(stream)))
+    return g
+
+
+def kv_epi_scores(g: torch.Tensor, n_a: int, window: int = 64, eps: float = 1e-6,
+                  detrend: bool = True, scores: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Eq. 3 (detrend) or eq. 2: band A (rows 0..n_a-1 of g) minus band B."""
+    _dev(g, torch.float32, "g")
+    if g.dim() != 2 or not 1 <= n_a < g.shape[0]:
+        raise ValueError("g must be [n_a + n_b, n] with both bands non-empty")
+    nl, n = g.shape
+    if scores is None:
+        scores = torch.empty(n, dtype=torch.float32, device=g.device)
+    _dev(scores, torch.float32, "scores")
+    if scores.numel() != n:
+        raise ValueError("scores must hold n entries")
+    _check("kv_epi_scores", _lib.load().kv_epi_scores(
+        _ptr(g), n_a, nl - n_a, n, window, float(eps), int(bool(detrend)), _ptr(scores),
+        _stream(stream)))
+    return scores
+
+
+def kv_select_tokens_workspace_bytes(n: int) -> int:
+    return int(_lib.load().kv_select_tokens_workspace_bytes(n))
+
+
+def kv_select_tokens(scores: torch.Tensor, k: int, idx: Optional[torch.Tensor] = None,
+                     stream=None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The k highest of n signed scores, ties to the lower position, ascending."""
+    _dev(scores, torch.float32, "scores")
+    n = scores.numel()
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=scores.device)
+    _dev(idx, torch.int32, "idx")
+    if idx.numel() < k:
+        raise ValueError("idx too small")
+    ws_bytes = kv_select_tokens_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    _dev(workspace, torch.uint8, "workspace")
+    if workspace.numel() < ws_bytes:
+        raise ValueError("workspace too small")
+    _check("kv_select_tokens", _lib.load().kv_select_tokens(
+        _ptr(scores), n, k, _ptr(idx), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return idx
+
+
+def kv_compact_tokens(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
+                      k_out: Optional[torch.Tensor] = None,
+                      v_out: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The same kept positions in every (layer, head): [L,H,n,d] -> [L,H,k,d]."""
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache")
+    _dev(idx, torch.int32, "idx")
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must both be [L,H,n,d]")
+    L, H, n, d = k_cache.shape
+    k = idx.numel()
+    shape = (L, H, k, d)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.bfloat16, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.bfloat16, device=k_cache.device)
+    _dev(k_out, torch.bfloat16, "k_out")
+    _dev(v_out, torch.bfloat16, "v_out")
+    if k_out.numel() < L * H * k * d or v_out.numel() < L * H * k * d:
+        raise ValueError("k_out / v_out too small")
+    _check("kv_compact_tokens", _lib.load().kv_compact_tokens(
+        _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(k_out), _ptr(v_out), L, H, d, n, k,
+        _stream(stream)))
+    return k_out, v_out
+
+
+def epikv_evict(h: torch.Tensor, n_a: int, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                budget: int, window: int = 64, eps: float = 1e-6, detrend: bool = True,
+                stream=None):
+    """Hidden-state deltas, band scores, top-`budget` tokens, token compaction:
+    returns (k_out, v_out, idx, scores, g)."""
+    g = kv_epi_deltas(h, stream=stream)
+    scores = kv_epi_scores(g, n_a, window, eps, detrend, stream=stream)
+    idx = kv_select_tokens(scores, budget, stream=stream)
+    k_out, v_out = kv_compact_tokens(k_cache, v_cache, idx, stream=stream)
+    return k_out, v_out, idx, scores, g
+
+
+# ---------------------------------------------------------------------------
 # the whole path
 # ---------------------------------------------------------------------------
 def score(q, k_ctx, k_new, scale=None, stream=None):

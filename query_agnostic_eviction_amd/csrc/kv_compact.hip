@@ -20,12 +20,15 @@ namespace {
 
 constexpr int kCpRows = 64;  // output rows per workgroup
 
-template <int D>
+// SHARED: one kept set idx[0..shared_k) for every head (token-level
+// eviction); output row t is head t / shared_k, entry t % shared_k, and the
+// offsets are not read.
+template <int D, bool SHARED>
 __global__ __launch_bounds__(256) void compact_kernel(
     const uint16_t* __restrict__ k_ctx, const uint16_t* __restrict__ v_ctx,
     const int64_t* __restrict__ offsets, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, int LH,
-    int64_t n_c, int64_t total) {
+    int64_t n_c, int64_t total, int64_t shared_k) {
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 256 / CPR;      // rows per pass of the block
   constexpr int IT = kCpRows / RPI;
@@ -37,14 +40,21 @@ __global__ __launch_bounds__(256) void compact_kernel(
     const int64_t t = t0 + threadIdx.x;
     int64_t r = -1;
     if (t < total) {
-      // head of row t: the largest lh with offsets[lh] <= t
-      int lo = 0, hi = LH - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offsets[mid] <= t) lo = mid; else hi = mid - 1;
+      int64_t lo, j;
+      if (SHARED) {
+        lo = t / shared_k;
+        j = idx[t - lo * shared_k];
+      } else {
+        // head of row t: the largest lh with offsets[lh] <= t
+        int a = 0, b = LH - 1;
+        while (a < b) {
+          const int mid = (a + b + 1) >> 1;
+          if (offsets[mid] <= t) a = mid; else b = mid - 1;
+        }
+        lo = a;
+        j = idx[t];
       }
-      const int64_t j = idx[t];
-      if (j >= 0 && j < n_c) r = (int64_t)lo * n_c + j;
+      if (j >= 0 && j < n_c) r = lo * n_c + j;
     }
     src_row[threadIdx.x] = r;
   }
@@ -75,13 +85,19 @@ template <int D>
 hipError_t launch_compact_d(const uint16_t* k_ctx, const uint16_t* v_ctx,
                             const int64_t* offsets, const int32_t* idx,
                             uint16_t* k_out, uint16_t* v_out, int LH,
-                            int64_t n_c, int64_t total, hipStream_t stream) {
+                            int64_t n_c, int64_t total, int64_t shared_k,
+                            hipStream_t stream) {
   const int64_t grid = (total + kCpRows - 1) / kCpRows;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel<D>, dim3((unsigned)grid), dim3(256), 0,
-                     stream, k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c,
-                     total);
+  if (shared_k > 0)
+    hipLaunchKernelGGL((compact_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c,
+                       total, shared_k);
+  else
+    hipLaunchKernelGGL((compact_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c,
+                       total, shared_k);
   return hipGetLastError();
 }
 
@@ -90,11 +106,12 @@ hipError_t launch_compact_d(const uint16_t* k_ctx, const uint16_t* v_ctx,
 hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
                           const int64_t* offsets, const int32_t* idx,
                           uint16_t* k_out, uint16_t* v_out, int LH, int d,
-                          int64_t n_c, int64_t total, hipStream_t stream) {
+                          int64_t n_c, int64_t total, int64_t shared_k,
+                          hipStream_t stream) {
   switch (d) {
-    case 64: return launch_compact_d<64>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
-    case 128: return launch_compact_d<128>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
-    case 256: return launch_compact_d<256>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, stream);
+    case 64: return launch_compact_d<64>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, shared_k, stream);
+    case 128: return launch_compact_d<128>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, shared_k, stream);
+    case 256: return launch_compact_d<256>(k_ctx, v_ctx, offsets, idx, k_out, v_out, LH, n_c, total, shared_k, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,6 +23,7 @@ namespace {
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkItems = 8;  // consecutive scores per thread per chunk
+constexpr int kHistBatch = 16;  // loads in flight per thread in a histogram pass
 
 // Exclusive prefix sum of x over the block; *total gets the block sum.
 __device__ __forceinline__ int block_excl_scan(int x, int* sm, int* total) {
@@ -51,6 +52,17 @@ __device__ __forceinline__ int block_excl_scan(int x, int* sm, int* total) {
   return before + v - x;
 }
 
+// Order-preserving map of a float's bits to uint32: identity for the
+// non-negative scores of the attention path; for signed scores the usual
+// sign flip, with -0.0 folded onto +0.0 so that equal values tie.
+template <bool SIGNED>
+__device__ __forceinline__ uint32_t sort_key(uint32_t v) {
+  if (!SIGNED) return v;
+  if (v == 0x80000000u) v = 0u;
+  return (v & 0x80000000u) ? ~v : (v | 0x80000000u);
+}
+
+template <bool SIGNED>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(
     const uint32_t* __restrict__ scores, int H, int n_c, int mode, int seg_len,
     int k, int nseg, int64_t* __restrict__ offsets, int32_t* __restrict__ idx) {
@@ -62,6 +74,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
   const int seg = blockIdx.x;
   const uint32_t* data = scores + (size_t)seg * seg_len;
   const int64_t out_base = (int64_t)seg * k;
+  const unsigned useg = (unsigned)seg_len;  // < 2^31: unsigned index math cannot wrap
 
   // ---- 1. radix select of the k-th largest bit pattern -------------------
   uint32_t prefix = 0, pmask = 0;
@@ -74,9 +87,21 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
     const int nb = 1 << widths[p];
     for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < seg_len; j += kTkThreads) {
-      const uint32_t v = data[j];
-      if ((v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & (nb - 1)], 1);
+    // kHistBatch independent loads in flight per thread, then the atomics
+    for (unsigned base = 0; base < useg; base += kTkThreads * kHistBatch) {
+      uint32_t v[kHistBatch];
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const unsigned j = base + u * kTkThreads + tid;
+        v[u] = j < useg ? data[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const unsigned j = base + u * kTkThreads + tid;
+        const uint32_t key = sort_key<SIGNED>(v[u]);
+        if (j < useg && (key & pmask) == prefix)
+          atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
+      }
     }
     __syncthreads();
     // thread t owns bins nb-1-2t and nb-2-2t (descending order)
@@ -103,20 +128,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
   const int need_eq = remaining;  // scores equal to T still to keep
 
   // ---- 2. ordered compaction ---------------------------------------------
-  if (mode == 0 && tid == 0) offsets[seg] = out_base;
-  if (seg == 0 && tid == 0) offsets[nseg * (mode == 0 ? 1 : H)] = (int64_t)nseg * k;
+  if (offsets != nullptr) {
+    if (mode == 0 && tid == 0) offsets[seg] = out_base;
+    if (seg == 0 && tid == 0) offsets[nseg * (mode == 0 ? 1 : H)] = (int64_t)nseg * k;
+  }
 
   int eq_seen = 0, kept_seen = 0;
 #pragma unroll 1
-  for (int base = 0; base < seg_len; base += kTkThreads * kTkItems) {
-    const int j0 = base + tid * kTkItems;
+  for (unsigned base = 0; base < useg; base += kTkThreads * kTkItems) {
+    const unsigned j0 = base + tid * kTkItems;
     uint32_t v[kTkItems];
     int neq = 0;
 #pragma unroll
     for (int i = 0; i < kTkItems; ++i) {
-      const int j = j0 + i;
-      v[i] = j < seg_len ? data[j] : 0u;
-      neq += (j < seg_len && v[i] == T) ? 1 : 0;
+      const unsigned j = j0 + i;
+      v[i] = j < useg ? sort_key<SIGNED>(data[j]) : 0u;
+      neq += (j < useg && v[i] == T) ? 1 : 0;
     }
     int eq_tot;
     const int eq_before = eq_seen + block_excl_scan(neq, sm, &eq_tot);
@@ -124,8 +151,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
     int nk = 0, e = 0;
 #pragma unroll
     for (int i = 0; i < kTkItems; ++i) {
-      const int j = j0 + i;
-      const bool valid = j < seg_len;
+      const unsigned j = j0 + i;
+      const bool valid = j < useg;
       const bool eq = valid && v[i] == T;
       keep[i] = valid && (v[i] > T || (eq && eq_before + e < need_eq));
       e += eq ? 1 : 0;
@@ -135,11 +162,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
     int pos = kept_seen + block_excl_scan(nk, sm, &k_tot);
 #pragma unroll
     for (int i = 0; i < kTkItems; ++i) {
-      const int j = j0 + i;
-      if (mode == 1 && j < seg_len && j % n_c == 0)
-        offsets[(int64_t)seg * H + j / n_c] = out_base + pos;
+      const unsigned j = j0 + i;
+      if (mode == 1 && j < useg && j % (unsigned)n_c == 0)
+        offsets[(int64_t)seg * H + j / (unsigned)n_c] = out_base + pos;
       if (keep[i]) {
-        if (pos < k) idx[out_base + pos] = mode == 1 ? j % n_c : j;
+        if (pos < k) idx[out_base + pos] = (int32_t)(mode == 1 ? j % (unsigned)n_c : j);
         ++pos;
       }
     }
@@ -149,154 +176,47 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Model-wide budget (mode 2): one top-k over all L*H*n_c scores, run as a
-// grid-wide radix select.  Every step is its own launch on the stream, with
-// the state in the caller's workspace:
-//   init  -> 3 x (histogram over the whole array, pick the bin)  -> T
-//   count (per block: scores > T and == T) -> scan over blocks -> ordered
-//   write (kept positions, CSR offsets at head boundaries).
+// Grid-wide select: one top-k over a long array spread over many workgroups
+// (the model-wide budget, mode 2, and the token budget).  The state lives in
+// the caller's workspace; the steps are stream-ordered launches, and within
+// a launch the last workgroup to finish (an atomic arrival counter, no
+// waiting) does the serial part:
+//   init -> 3 x hist (last block: pick the bin, clear the histogram)
+//        -> count (last block: scan the per-block counts) -> ordered write.
 // ---------------------------------------------------------------------------
 constexpr int kGThreads = 256;
 constexpr int kGItems = 16;                  // scores per thread per chunk
 constexpr int kGChunk = kGThreads * kGItems;
+constexpr int kGMaxBlocks = 1024;            // bound of the count scan
 
 struct GlobalState {
   unsigned long long hist[2048];
   unsigned long long remaining;  // scores equal to the prefix still to keep
   unsigned int prefix, pmask;
+  unsigned int arrived;          // workgroups done in the current launch
 };
 
-__global__ void gsel_init(GlobalState* st, long long k, int64_t* offsets, int nheads) {
-  for (int i = threadIdx.x; i < 2048; i += blockDim.x) st->hist[i] = 0;
-  if (threadIdx.x == 0) {
-    st->remaining = (unsigned long long)k;
-    st->prefix = 0;
-    st->pmask = 0;
-    offsets[nheads] = k;
-  }
+__device__ __forceinline__ unsigned long long load_agent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kGThreads) void gsel_hist(const uint32_t* __restrict__ data,
-                                                       long long n, long long per_block,
-                                                       GlobalState* st, int shift, int width) {
-  __shared__ unsigned int h[2048];
-  for (int i = threadIdx.x; i < 2048; i += kGThreads) h[i] = 0;
-  __syncthreads();
-  const unsigned int prefix = st->prefix, pmask = st->pmask, nb = 1u << width;
-  const long long b0 = (long long)blockIdx.x * per_block;
-  const long long b1 = b0 + per_block < n ? b0 + per_block : n;
-  for (long long j = b0 + threadIdx.x; j < b1; j += kGThreads) {
-    const uint32_t v = data[j];
-    if ((v & pmask) == prefix) atomicAdd(&h[(v >> shift) & (nb - 1)], 1u);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < (int)nb; i += kGThreads)
-    if (h[i]) atomicAdd(&st->hist[i], (unsigned long long)h[i]);
-}
-
-// One block of 1024 threads: the bin that holds the remaining-th largest.
-__global__ __launch_bounds__(kTkThreads) void gsel_pick(GlobalState* st, int shift, int width) {
-  __shared__ unsigned long long wsum[kTkWaves];
-  __shared__ unsigned long long sel[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb = 1 << width;
-  const unsigned long long rem = st->remaining;
-  // thread t owns bins nb-1-2t and nb-2-2t (descending); 64-bit prefix sums
-  const int b_hi = nb - 1 - 2 * tid, b_lo = b_hi - 1;
-  const unsigned long long h_hi = b_hi >= 0 ? st->hist[b_hi] : 0;
-  const unsigned long long h_lo = b_lo >= 0 ? st->hist[b_lo] : 0;
-  unsigned long long v = h_hi + h_lo, x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  unsigned long long before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  const unsigned long long above = before + x - v;
-  if (b_hi >= 0 && above < rem && rem <= above + h_hi) { sel[0] = b_hi; sel[1] = above; }
-  if (b_lo >= 0 && above + h_hi < rem && rem <= above + h_hi + h_lo) { sel[0] = b_lo; sel[1] = above + h_hi; }
-  __syncthreads();
-  if (tid == 0) {
-    st->prefix |= (unsigned int)sel[0] << shift;
-    st->pmask |= (unsigned int)(nb - 1) << shift;
-    st->remaining = rem - sel[1];
-  }
-  // clear the histogram for the next pass
-  for (int i = tid; i < 2048; i += kTkThreads) st->hist[i] = 0;
-}
-
-__global__ __launch_bounds__(kGThreads) void gsel_count(const uint32_t* __restrict__ data,
-                                                        long long n, long long per_block,
-                                                        const GlobalState* st,
-                                                        unsigned long long* counts) {
-  __shared__ unsigned long long red[2][kGThreads / kWave];
-  const uint32_t T = st->prefix;
-  const long long b0 = (long long)blockIdx.x * per_block;
-  const long long b1 = b0 + per_block < n ? b0 + per_block : n;
-  unsigned long long eq = 0, gt = 0;
-  for (long long j = b0 + threadIdx.x; j < b1; j += kGThreads) {
-    const uint32_t v = data[j];
-    eq += v == T;
-    gt += v > T;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    eq += __shfl_xor(eq, o);
-    gt += __shfl_xor(gt, o);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) { red[0][wave] = eq; red[1][wave] = gt; }
+// True in every thread of the workgroup that arrives last in this launch.
+// The barrier completes every wave's writes to this die's L2; one
+// device-scope fence (an L2 write-back on a multi-die part) then publishes
+// them before the arrival is counted.  The last workgroup reads what the
+// others published through device-scope loads.
+__device__ __forceinline__ bool last_to_arrive(GlobalState* st) {
+  __shared__ int last;
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned long long e = 0, g = 0;
-    for (int w = 0; w < kGThreads / kWave; ++w) { e += red[0][w]; g += red[1][w]; }
-    counts[2 * blockIdx.x] = e;
-    counts[2 * blockIdx.x + 1] = g;
+    __threadfence();
+    last = atomicAdd(&st->arrived, 1u) == gridDim.x - 1;
   }
-}
-
-// Inclusive prefix sum of x over a 1024-thread block (64-bit).
-__device__ __forceinline__ unsigned long long block_incl_scan1024(unsigned long long x,
-                                                                  unsigned long long* sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) sm[wave] = v;
   __syncthreads();
-  unsigned long long before = 0;
-  for (int w = 0; w < wave; ++w) before += sm[w];
-  __syncthreads();
-  return before + v;
+  return last;
 }
 
-// One block of 1024 threads, one write-pass block per thread (there are at
-// most 1024): turns the per-block counts into the number of equal scores and
-// of kept scores before each block.
-__global__ __launch_bounds__(kTkThreads) void gsel_scan(const GlobalState* st,
-                                                        unsigned long long* counts,
-                                                        int nblocks) {
-  __shared__ unsigned long long sm[kTkWaves];
-  const int b = threadIdx.x;
-  const unsigned long long need = st->remaining;
-  const unsigned long long e = b < nblocks ? counts[2 * b] : 0;
-  const unsigned long long g = b < nblocks ? counts[2 * b + 1] : 0;
-  const unsigned long long eq_before = block_incl_scan1024(e, sm) - e;
-  const unsigned long long take =
-      eq_before >= need ? 0 : (need - eq_before < e ? need - eq_before : e);
-  const unsigned long long kept_before = block_incl_scan1024(g + take, sm) - (g + take);
-  if (b < nblocks) {
-    counts[2 * b] = eq_before;
-    counts[2 * b + 1] = kept_before;
-  }
-}
-
+// Exclusive prefix sum over a 256-thread block (64-bit); *total = block sum.
 __device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long long x,
                                                                  unsigned long long* sm,
                                                                  unsigned long long* total) {
@@ -319,9 +239,160 @@ __device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long lo
   return before + v - x;
 }
 
+__global__ void gsel_init(GlobalState* st, long long k, int64_t* offsets, int nheads) {
+  for (int i = threadIdx.x; i < 2048; i += blockDim.x) st->hist[i] = 0;
+  if (threadIdx.x == 0) {
+    st->remaining = (unsigned long long)k;
+    st->prefix = 0;
+    st->pmask = 0;
+    st->arrived = 0;
+    if (offsets) offsets[nheads] = k;
+  }
+}
+
+template <bool SIGNED>
+__global__ __launch_bounds__(kGThreads) void gsel_hist(const uint32_t* __restrict__ data,
+                                                       long long n, long long per_block,
+                                                       GlobalState* st, int shift, int width) {
+  __shared__ unsigned int h[2048];
+  __shared__ unsigned long long sm[kGThreads / kWave];
+  __shared__ unsigned long long sel[2];
+  for (int i = threadIdx.x; i < 2048; i += kGThreads) h[i] = 0;
+  __syncthreads();
+  const unsigned int prefix = st->prefix, pmask = st->pmask, nb = 1u << width;
+  const long long b0 = (long long)blockIdx.x * per_block;
+  const long long b1 = b0 + per_block < n ? b0 + per_block : n;
+  for (long long base = b0; base < b1; base += kGChunk) {
+    uint32_t v[kGItems];
+#pragma unroll
+    for (int u = 0; u < kGItems; ++u) {
+      const long long j = base + u * kGThreads + threadIdx.x;
+      v[u] = j < b1 ? data[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kGItems; ++u) {
+      const long long j = base + u * kGThreads + threadIdx.x;
+      const uint32_t key = sort_key<SIGNED>(v[u]);
+      if (j < b1 && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (int)nb; i += kGThreads)
+    if (h[i]) atomicAdd(&st->hist[i], (unsigned long long)h[i]);
+  if (!last_to_arrive(st)) return;
+
+  // last workgroup: the bin holding the remaining-th largest key; thread t
+  // owns the 8 bins nb-1-8t .. nb-8-8t (descending)
+  const unsigned long long rem = st->remaining;
+  unsigned long long c[8], tot8 = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int b = (int)nb - 1 - 8 * (int)threadIdx.x - u;
+    c[u] = b >= 0 ? load_agent(&st->hist[b]) : 0ull;
+    tot8 += c[u];
+  }
+  unsigned long long all;
+  unsigned long long above = block_excl_scan64(tot8, sm, &all);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int b = (int)nb - 1 - 8 * (int)threadIdx.x - u;
+    if (b >= 0 && above < rem && rem <= above + c[u]) { sel[0] = (unsigned)b; sel[1] = above; }
+    above += c[u];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2048; i += kGThreads) st->hist[i] = 0;
+  if (threadIdx.x == 0) {
+    st->prefix = prefix | ((unsigned int)sel[0] << shift);
+    st->pmask = pmask | ((nb - 1) << shift);
+    st->remaining = rem - sel[1];
+    st->arrived = 0;
+  }
+}
+
+// Per block: scores equal to / above the selected key; the last block turns
+// them into the equal and kept counts before each block.
+template <bool SIGNED>
+__global__ __launch_bounds__(kGThreads) void gsel_count(const uint32_t* __restrict__ data,
+                                                        long long n, long long per_block,
+                                                        GlobalState* st,
+                                                        unsigned long long* counts) {
+  __shared__ unsigned long long red[2][kGThreads / kWave];
+  __shared__ unsigned long long sm[kGThreads / kWave];
+  const uint32_t T = st->prefix;
+  const long long b0 = (long long)blockIdx.x * per_block;
+  const long long b1 = b0 + per_block < n ? b0 + per_block : n;
+  unsigned long long eq = 0, gt = 0;
+  for (long long base = b0; base < b1; base += kGChunk) {
+    uint32_t v[kGItems];
+#pragma unroll
+    for (int u = 0; u < kGItems; ++u) {
+      const long long j = base + u * kGThreads + threadIdx.x;
+      v[u] = j < b1 ? data[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kGItems; ++u) {
+      const long long j = base + u * kGThreads + threadIdx.x;
+      const uint32_t key = sort_key<SIGNED>(v[u]);
+      eq += (j < b1 && key == T) ? 1 : 0;
+      gt += (j < b1 && key > T) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    eq += __shfl_xor(eq, o);
+    gt += __shfl_xor(gt, o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = eq; red[1][wave] = gt; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long e = 0, g = 0;
+    for (int w = 0; w < kGThreads / kWave; ++w) { e += red[0][w]; g += red[1][w]; }
+    counts[2 * blockIdx.x] = e;
+    counts[2 * blockIdx.x + 1] = g;
+  }
+  if (!last_to_arrive(st)) return;
+
+  // last workgroup: thread t owns blocks 4t .. 4t+3 (gridDim.x <= 1024)
+  const int nblocks = (int)gridDim.x;
+  const unsigned long long need = st->remaining;
+  unsigned long long e[4], g[4], e_sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int b = 4 * (int)threadIdx.x + u;
+    e[u] = b < nblocks ? load_agent(&counts[2 * b]) : 0ull;
+    g[u] = b < nblocks ? load_agent(&counts[2 * b + 1]) : 0ull;
+    e_sum += e[u];
+  }
+  unsigned long long tot;
+  unsigned long long eq_before = block_excl_scan64(e_sum, sm, &tot);
+  unsigned long long kept[4], k_sum = 0, eqb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    eqb[u] = eq_before;
+    const unsigned long long take =
+        eq_before >= need ? 0 : (need - eq_before < e[u] ? need - eq_before : e[u]);
+    kept[u] = g[u] + take;
+    k_sum += kept[u];
+    eq_before += e[u];
+  }
+  unsigned long long kept_before = block_excl_scan64(k_sum, sm, &tot);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int b = 4 * (int)threadIdx.x + u;
+    if (b < nblocks) {
+      counts[2 * b] = eqb[u];
+      counts[2 * b + 1] = kept_before;
+    }
+    kept_before += kept[u];
+  }
+  if (threadIdx.x == 0) st->arrived = 0;
+}
+
+template <bool SIGNED>
 __global__ __launch_bounds__(kGThreads) void gsel_write(const uint32_t* __restrict__ data,
                                                         long long n, long long per_block,
-                                                        int n_c, const GlobalState* st,
+                                                        long long n_c, const GlobalState* st,
                                                         const unsigned long long* counts,
                                                         int64_t* __restrict__ offsets,
                                                         int32_t* __restrict__ idx,
@@ -340,7 +411,7 @@ __global__ __launch_bounds__(kGThreads) void gsel_write(const uint32_t* __restri
 #pragma unroll
     for (int i = 0; i < kGItems; ++i) {
       const long long j = j0 + i;
-      v[i] = j < b1 ? data[j] : 0u;
+      v[i] = j < b1 ? sort_key<SIGNED>(data[j]) : 0u;
       neq += (j < b1 && v[i] == T) ? 1 : 0;
     }
     unsigned long long eq_tot;
@@ -361,7 +432,7 @@ __global__ __launch_bounds__(kGThreads) void gsel_write(const uint32_t* __restri
 #pragma unroll
     for (int i = 0; i < kGItems; ++i) {
       const long long j = j0 + i;
-      if (j < b1 && j % n_c == 0) offsets[j / n_c] = (int64_t)pos;
+      if (offsets && j < b1 && j % n_c == 0) offsets[j / n_c] = (int64_t)pos;
       if (keep[i]) {
         if ((long long)pos < k) idx[pos] = (int32_t)(j % n_c);
         ++pos;
@@ -402,25 +473,26 @@ __global__ __launch_bounds__(256) void head_max_kernel(const float* __restrict__
 
 }  // namespace
 
-size_t global_select_workspace(long long n) {
-  const long long per_block = global_select_per_block(n);
-  const long long nblocks = (n + per_block - 1) / per_block;
-  return sizeof(GlobalState) + 16 * (size_t)nblocks + 256;
-}
-
 long long global_select_per_block(long long n) {
-  // about 4 blocks per CU, each a whole number of write-pass chunks
-  long long per = (n + 1023) / 1024;
+  // a whole number of chunks per block, at most kGMaxBlocks blocks
+  long long per = (n + kGMaxBlocks - 1) / kGMaxBlocks;
   per = (per + kGChunk - 1) / kGChunk * kGChunk;
   return per < kGChunk ? kGChunk : per;
 }
 
-hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nheads,
-                              long long k, int64_t* offsets, int32_t* idx,
-                              void* workspace, hipStream_t stream) {
+size_t global_select_workspace(long long n) {
+  const long long per_block = global_select_per_block(n);
+  const long long nblocks = (n + per_block - 1) / per_block;
+  return ((sizeof(GlobalState) + 255) / 256) * 256 + 16 * (size_t)nblocks;
+}
+
+template <bool SIGNED>
+static hipError_t launch_global_select(const float* scores, long long n, long long n_c,
+                                       int nheads, long long k, int64_t* offsets,
+                                       int32_t* idx, void* workspace, hipStream_t stream) {
   const long long per_block = global_select_per_block(n);
   const long long nblocks_ll = (n + per_block - 1) / per_block;
-  if (n < 1 || nblocks_ll > kTkThreads) return hipErrorInvalidValue;  // gsel_scan's limit
+  if (n < 1 || nblocks_ll > kGMaxBlocks) return hipErrorInvalidValue;
   const int nblocks = (int)nblocks_ll;
   GlobalState* st = reinterpret_cast<GlobalState*>(workspace);
   unsigned long long* counts = reinterpret_cast<unsigned long long*>(
@@ -428,18 +500,26 @@ hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nhe
   const uint32_t* data = reinterpret_cast<const uint32_t*>(scores);
   hipLaunchKernelGGL(gsel_init, dim3(1), dim3(256), 0, stream, st, k, offsets, nheads);
   const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
-  for (int p = 0; p < 3; ++p) {
-    hipLaunchKernelGGL(gsel_hist, dim3(nblocks), dim3(kGThreads), 0, stream, data, n,
-                       per_block, st, shifts[p], widths[p]);
-    hipLaunchKernelGGL(gsel_pick, dim3(1), dim3(kTkThreads), 0, stream, st, shifts[p],
-                       widths[p]);
-  }
-  hipLaunchKernelGGL(gsel_count, dim3(nblocks), dim3(kGThreads), 0, stream, data, n,
+  for (int p = 0; p < 3; ++p)
+    hipLaunchKernelGGL(gsel_hist<SIGNED>, dim3(nblocks), dim3(kGThreads), 0, stream, data,
+                       n, per_block, st, shifts[p], widths[p]);
+  hipLaunchKernelGGL(gsel_count<SIGNED>, dim3(nblocks), dim3(kGThreads), 0, stream, data, n,
                      per_block, st, counts);
-  hipLaunchKernelGGL(gsel_scan, dim3(1), dim3(kTkThreads), 0, stream, st, counts, nblocks);
-  hipLaunchKernelGGL(gsel_write, dim3(nblocks), dim3(kGThreads), 0, stream, data, n,
+  hipLaunchKernelGGL(gsel_write<SIGNED>, dim3(nblocks), dim3(kGThreads), 0, stream, data, n,
                      per_block, n_c, st, counts, offsets, idx, k);
   return hipGetLastError();
+}
+
+hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nheads,
+                              long long k, int64_t* offsets, int32_t* idx,
+                              void* workspace, hipStream_t stream) {
+  return launch_global_select<false>(scores, n, n_c, nheads, k, offsets, idx, workspace,
+                                     stream);
+}
+
+hipError_t launch_select_tokens_grid(const float* scores, long long n, long long k,
+                                     int32_t* idx, void* workspace, hipStream_t stream) {
+  return launch_global_select<true>(scores, n, n, 1, k, nullptr, idx, workspace, stream);
 }
 
 hipError_t launch_head_max(const float* scores, int nheads, int n_c, float* out,
@@ -453,10 +533,11 @@ hipError_t launch_topk(const float* scores, int L, int H, int n_c, int mode,
                        hipStream_t stream) {
   const int nseg = mode == 0 ? L * H : L;
   const int seg_len = mode == 0 ? n_c : H * n_c;
-  hipLaunchKernelGGL(topk_kernel, dim3(nseg), dim3(kTkThreads), 0, stream,
+  hipLaunchKernelGGL(topk_kernel<false>, dim3(nseg), dim3(kTkThreads), 0, stream,
                      reinterpret_cast<const uint32_t*>(scores), H, n_c, mode,
                      seg_len, (int)k_per_segment, nseg, offsets, idx);
   return hipGetLastError();
 }
+
 
 }  // namespace kvq

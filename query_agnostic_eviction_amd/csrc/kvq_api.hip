@@ -281,7 +281,65 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
   return hip_status(kvq::launch_compact(
       static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx),
       offsets, idx, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
-      L * H, d, n_c, total, static_cast<hipStream_t>(stream)));
+      L * H, d, n_c, total, 0, static_cast<hipStream_t>(stream)));
+}
+
+int kv_epi_deltas(const void* h, int n_layers, int64_t n, int D, float* g, void* stream) {
+  if (!h || !g || n_layers < 1 || n < 1) return KV_ERR_INVALID_ARG;
+  if (D < 8 || D > 8192 || D % 8 != 0) return KV_ERR_UNSUPPORTED;
+  if (n >= (int64_t)1 << 36) return KV_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(g, 4)) return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_epi_deltas(static_cast<const uint16_t*>(h), n_layers, n, D, g,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int kv_epi_scores(const float* g, int n_a, int n_b, int64_t n, int window, double eps,
+                  int detrend, float* scores, void* stream) {
+  if (!g || !scores || n_a < 1 || n_b < 1 || n < 1 || window < 1) return KV_ERR_INVALID_ARG;
+  if (!(eps > 0.0) || !isfinite(eps) || (detrend != 0 && detrend != 1))
+    return KV_ERR_INVALID_ARG;
+  if (window > 1024) return KV_ERR_UNSUPPORTED;
+  if ((int64_t)n_a + n_b > 4096 || n >= (int64_t)1 << 36) return KV_ERR_INVALID_ARG;
+  if (!aligned(g, 4) || !aligned(scores, 4)) return KV_ERR_ALIGNMENT;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_epi_scores(g, n_a, n_b, n, window, eps, detrend, scores,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_select_tokens_workspace_bytes(int64_t n) {
+  if (n < 1) return 0;
+  return kvq::global_select_workspace(n);
+}
+
+int kv_select_tokens(const float* scores, int64_t n, int64_t k, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scores || !idx || !workspace || n < 1 || k < 1 || k > n) return KV_ERR_INVALID_ARG;
+  if (n >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  if (!aligned(scores, 4) || !aligned(idx, 4) || !aligned(workspace, 256))
+    return KV_ERR_ALIGNMENT;
+  if (workspace_bytes < kv_select_tokens_workspace_bytes(n)) return KV_ERR_CAPACITY;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_select_tokens_grid(scores, n, k, idx, workspace,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int kv_compact_tokens(const void* k_cache, const void* v_cache, const int32_t* idx,
+                      void* k_out, void* v_out, int L, int H, int d, int64_t n, int64_t k,
+                      void* stream) {
+  if (!k_cache || !v_cache || !idx || !k_out || !v_out) return KV_ERR_INVALID_ARG;
+  if (L < 1 || H < 1 || n < 1 || k < 0 || k > n) return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31 || n >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_out, 16) ||
+      !aligned(v_out, 16) || !aligned(idx, 4))
+    return KV_ERR_ALIGNMENT;
+  if (k == 0) return KV_OK;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_compact(
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), nullptr,
+      idx, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), L * H, d, n,
+      (int64_t)L * H * k, k, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

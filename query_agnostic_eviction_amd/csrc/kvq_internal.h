@@ -73,9 +73,22 @@ hipError_t launch_head_max(const float* scores, int nheads, int n_c, float* out,
                            hipStream_t stream);
 
 // Gather of kept rows; see kv_compact.
+// shared_k > 0: one kept set of shared_k positions for every head, no offsets.
 hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
                           const int64_t* offsets, const int32_t* idx,
                           uint16_t* k_out, uint16_t* v_out, int LH, int d,
-                          int64_t n_c, int64_t total, hipStream_t stream);
+                          int64_t n_c, int64_t total, int64_t shared_k,
+                          hipStream_t stream);
+
+// Top-k of n signed finite floats (ties to the lower index), ascending, by
+// the grid-wide select (workspace of global_select_workspace(n) bytes).
+hipError_t launch_select_tokens_grid(const float* scores, long long n, long long k,
+                                     int32_t* idx, void* workspace, hipStream_t stream);
+
+// EpiKV token score: hidden-state change norms, then band statistics.
+hipError_t launch_epi_deltas(const uint16_t* h, int n_layers, int64_t n, int D, float* g,
+                             hipStream_t stream);
+hipError_t launch_epi_scores(const float* g, int n_a, int n_b, int64_t n, int w, double eps,
+                             int detrend, float* scores, hipStream_t stream);
 
 }  // namespace kvq

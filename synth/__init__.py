@@ -9,3 +9,5 @@ from .generate import (bf16_bits_to_f32, chunk_rows, default_workers,
                        f64_to_bf16_bits, generate_chunked_head,
                        generate_chunked_workload, generate_head,
                        generate_workload)
+from .epikv import (EPI_ALL, EPI_BY_NAME, EPIKV_R1_8B_64K, EPIKV_TINY, EpiWorkload,
+                    generate_hidden, generate_hidden_layer, generate_kv)

@@ -216,3 +216,49 @@ def test_chunked_validation(lib, name):
     assert call(n_c=0) == INV
     assert call(scale=math.nan) == INV
     assert call(q=P2) == ALN
+
+
+def test_epikv_validation(lib):
+    d = lib.kv_epi_deltas
+    assert d(NUL, 2, 100, 4096, P, NUL) == INV
+    assert d(P, 2, 100, 4096, NUL, NUL) == INV
+    assert d(P, 0, 100, 4096, P, NUL) == INV
+    assert d(P, 2, 0, 4096, P, NUL) == INV
+    for D in (0, 4, 12, 8200, 16384):
+        assert d(P, 2, 100, D, P, NUL) == UNS
+    assert d(P2, 2, 100, 4096, P, NUL) == ALN
+    assert d(P, 2, 100, 4096, P2, NUL) == ALN
+
+    s = lib.kv_epi_scores
+    assert s(NUL, 1, 1, 100, 64, 1e-6, 1, P, NUL) == INV
+    assert s(P, 0, 1, 100, 64, 1e-6, 1, P, NUL) == INV
+    assert s(P, 1, 0, 100, 64, 1e-6, 1, P, NUL) == INV
+    assert s(P, 1, 1, 0, 64, 1e-6, 1, P, NUL) == INV
+    assert s(P, 1, 1, 100, 0, 1e-6, 1, P, NUL) == INV
+    assert s(P, 1, 1, 100, 1025, 1e-6, 1, P, NUL) == UNS
+    for eps in (0.0, -1e-6, math.nan, math.inf):
+        assert s(P, 1, 1, 100, 64, eps, 1, P, NUL) == INV
+    assert s(P, 1, 1, 100, 64, 1e-6, 2, P, NUL) == INV
+    assert s(P2, 1, 1, 100, 64, 1e-6, 1, P, NUL) == ALN
+
+    t = lib.kv_select_tokens
+    wsb = lib.kv_select_tokens_workspace_bytes(100)
+    assert wsb >= 16384 and lib.kv_select_tokens_workspace_bytes(0) == 0
+    assert lib.kv_select_tokens_workspace_bytes(65536) == wsb + 16 * 15   # a block per 4096
+    assert t(NUL, 100, 10, P, P, wsb, NUL) == INV
+    assert t(P, 100, 0, P, P, wsb, NUL) == INV
+    assert t(P, 100, 101, P, P, wsb, NUL) == INV
+    assert t(P, 100, 10, P, NUL, wsb, NUL) == INV
+    assert t(P, 2 ** 31, 10, P, P, wsb, NUL) == INV
+    assert t(P, 100, 10, P2, P, wsb, NUL) == ALN
+    assert t(P, 100, 10, P, ctypes.c_void_p(0x10080), wsb, NUL) == ALN
+    assert t(P, 100, 10, P, P, wsb - 1, NUL) == CAP
+
+    c = lib.kv_compact_tokens
+    assert c(NUL, P, P, P, P, 2, 2, 128, 100, 10, NUL) == INV
+    assert c(P, P, P, P, P, 2, 2, 128, 100, 101, NUL) == INV
+    assert c(P, P, P, P, P, 2, 2, 128, 100, -1, NUL) == INV
+    assert c(P, P, P, P, P, 2, 2, 96, 100, 10, NUL) == UNS
+    assert c(P, P, P, P4, P, 2, 2, 128, 100, 10, NUL) == ALN
+    assert c(P, P, P2, P, P, 2, 2, 128, 100, 10, NUL) == ALN
+    assert c(P, P, P, P, P, 2, 2, 128, 100, 0, NUL) == OK      # nothing to copy, no launch
