@@ -114,7 +114,7 @@ def synth_total(w, mode):
     return w.L * kl
 
 
-def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None):
+def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None, merge=False):
     """The float64 oracle on whole heads of the workload, head after head,
     until `seconds` have passed (at least one head)."""
     import oracle
@@ -131,7 +131,13 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None):
         else:
             S, _ = oracle.head_scores_parallel(q, kc, kn, float(w.scale), workers=workers)
         off, idx = oracle.select(S[None, None], w.keep_ratio, 0)
-        oracle.compact(gen["k_ctx"][None, None], gen["v_ctx"][None, None], off, idx)
+        if merge:
+            so, si = synth.nearest_position_routes(off, idx, w.n_c)
+            oracle.selkv.merge_compact(oracle.bf16_to_f64(gen["k_ctx"])[None, None],
+                                       oracle.bf16_to_f64(gen["v_ctx"])[None, None],
+                                       off, idx, so, si)
+        else:
+            oracle.compact(gen["k_ctx"][None, None], gen["v_ctx"][None, None], off, idx)
         t_oracle += time.perf_counter() - t0
         done += w.n_c
         heads.append((l, h))
@@ -144,7 +150,7 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None):
         "kind": "oracle",
         "sample": f"{len(heads)} whole (layer, KV head) slices of {w.name} "
                   f"({done} context KV pairs): float64 attention rows, max score, "
-                  f"top-k and gather; {t_oracle:.1f} s",
+                  f"top-k and {'gated merge' if merge else 'gather'}; {t_oracle:.1f} s",
     }
 
 
@@ -158,6 +164,9 @@ def main():
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked scoring with this chunk length (0 = whole context)")
+    ap.add_argument("--merge", action="store_true",
+                    help="gated merge (soft cosine gate) of the evicted tokens into their "
+                         "nearest kept position instead of plain compaction")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget for the CPU baseline (0 = skip)")
     args = ap.parse_args()
@@ -185,7 +194,7 @@ def main():
     print(f"# generated {w.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds, args.mode, chunk)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.mode, chunk, args.merge)
         print(f"# cpu baseline: {cpu['value']:.3g} pairs/s", file=sys.stderr, flush=True)
 
     import torch
@@ -212,7 +221,10 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    names = ("kvscore_lse", "kvscore_colmax", "kv_topk_select", "kv_compact")
+    names = ("kvscore_lse", "kvscore_colmax", "kv_topk_select",
+             "kv_merge_compact" if args.merge else "kv_compact")
+    route = {}
+    gate = mass = None
 
     def step(ev=None):
         def mark(i):
@@ -233,13 +245,28 @@ def main():
         mark(2)
         kvq.kv_topk_select(scores, w.keep_ratio, args.mode, offsets, idx, stream, ws)
         mark(3)
-        kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, k_out, v_out, stream)
+        if route:
+            kvq.kv_merge_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, route["so"],
+                                 route["si"], k_out, v_out, gate, mass, stream)
+        else:
+            kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, k_out, v_out, stream)
         mark(4)
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, 1 if args.merge else 0)):
         step()
         torch.cuda.synchronize()
         print(f"# warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+        if args.merge and not route:
+            # routing is an input of the merge: built once on the host from the
+            # kept set (identical in every step: same inputs, same scores)
+            so, si = synth.nearest_position_routes(offsets.cpu().numpy(), idx.cpu().numpy(),
+                                                   n_c)
+            route["so"] = torch.from_numpy(so).cuda()
+            route["si"] = torch.from_numpy(si).cuda()
+            gate = torch.empty(max(si.size, 1), dtype=torch.float32, device="cuda")
+            mass = torch.empty(total, dtype=torch.float32, device="cuda")
+            work["merge_bytes"] = (2.0 * 2 * d * (total + si.size) + 2.0 * 2 * d * total
+                                   + 8.0 * si.size + 12.0 * total + 8.0 * (L * H + 1))
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
               for _ in range(args.steps)]
@@ -263,7 +290,9 @@ def main():
     col_tf = work["colmax_flops"] / (ms["kvscore_colmax"] * 1e-3) / 1e12
     scoring_tf = (work["lse_flops"] + work["colmax_flops"]) / (
         (ms["kvscore_lse"] + ms["kvscore_colmax"]) * 1e-3) / 1e12
-    cmp_gbs = work["compact_bytes"] / (ms["kv_compact"] * 1e-3) / 1e9
+    cmp_name = names[3]
+    cmp_gbs = work["merge_bytes" if args.merge else "compact_bytes"] / (
+        ms[cmp_name] * 1e-3) / 1e9
     sel_gbs = work["select_bytes"] / (ms["kv_topk_select"] * 1e-3) / 1e9
 
     dominant = max(names, key=lambda n: ms[n])
@@ -274,7 +303,7 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
     else:
-        achieved = cmp_gbs if dominant == "kv_compact" else sel_gbs
+        achieved = cmp_gbs if dominant == cmp_name else sel_gbs
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
@@ -294,7 +323,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "L": L, "H": H, "G": G, "d": d, "n_c": n_c,
                    "n_prompt": w.n_prompt, "keep_ratio": w.keep_ratio,
-                   "select_mode": args.mode, "chunk": chunk},
+                   "select_mode": args.mode, "chunk": chunk,
+                   "merge": "soft cosine gate, nearest kept position" if args.merge else None},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v, 4) for n, v in ms.items()},

@@ -181,6 +181,28 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream);
 
+/* Gated merge instead of drop (page "Selective KV cache merging", section
+ * 1: the soft cosine gate).  For kept row t (head lh with offsets[lh] <= t <
+ * offsets[lh+1], position idx[t]) and every routed position j listed in
+ * src_idx[src_offsets[t] .. src_offsets[t+1]) (positions of the same head):
+ *   g_j  = max(<v_j, v_t> / (|v_j| |v_t|), 0)   (0 if a norm is 0 or j is
+ *          outside [0, n_c))
+ *   k_out[t] = (k_t + sum_j g_j k_j) / (1 + sum_j g_j), v_out likewise,
+ * summed in fp32 in list order and rounded to bf16 (nearest-even);
+ * gate[s] = g of entry s (n_src floats) and mass[t] = sum_j g_j (total
+ * floats), each skipped when its pointer is NULL.  The page stops before
+ * its routing and merge sections, so the routing is the caller's (any rule
+ * producing the lists) and the merge is read as this weighted mean; with
+ * every list empty the call equals kv_compact.  src_offsets int64 [total+1]
+ * non-decreasing from 0 to n_src (ranges are clamped to [0, n_src)); kept
+ * rows with an index outside [0, n_c) come out as zeros.  d in
+ * {64, 128, 256}. */
+int kv_merge_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
+                     const int32_t* idx, const int64_t* src_offsets,
+                     const int32_t* src_idx, void* k_out, void* v_out, float* gate,
+                     float* mass, int L, int H, int d, int64_t n_c, int64_t total,
+                     int64_t n_src, void* stream);
+
 /* ------------------------------------------------------------------------
  * Attention-free token score (page "EpiKV", section 3.2, equations 1-3) and
  * token-level eviction under a budget of K tokens (section 3.1).  No

@@ -21,7 +21,7 @@ EXPORTS = (
     "kvscore_chunked_colmax", "kv_topk_total", "kv_topk_workspace_bytes",
     "kv_topk_select", "kv_head_scores", "kv_compact", "kv_epi_deltas",
     "kv_epi_scores", "kv_select_tokens_workspace_bytes", "kv_select_tokens",
-    "kv_compact_tokens",
+    "kv_compact_tokens", "kv_merge_compact",
 )
 
 _lib = None
@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
         "kv_select_tokens_workspace_bytes": (sz, [i64]),
         "kv_select_tokens": (i32, [vp, i64, i64, vp, vp, sz, vp]),
         "kv_compact_tokens": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, vp]),
+        "kv_merge_compact": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                   i64, i64, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

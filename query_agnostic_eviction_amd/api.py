@@ -271,6 +271,45 @@ def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
     return k_out, v_out
 
 
+def kv_merge_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
+                     idx: torch.Tensor, src_offsets: torch.Tensor, src_idx: torch.Tensor,
+                     k_out: Optional[torch.Tensor] = None,
+                     v_out: Optional[torch.Tensor] = None,
+                     gate: Optional[torch.Tensor] = None,
+                     mass: Optional[torch.Tensor] = None, stream=None):
+    """SelKV soft cosine gate and gated merge of routed tokens into the kept
+    rows: returns (k_out, v_out, gate, mass)."""
+    _dev(k_ctx, torch.bfloat16, "k_ctx")
+    _dev(v_ctx, torch.bfloat16, "v_ctx")
+    for t, name, dt in ((offsets, "offsets", torch.int64), (idx, "idx", torch.int32),
+                        (src_offsets, "src_offsets", torch.int64),
+                        (src_idx, "src_idx", torch.int32)):
+        _dev(t, dt, name)
+    if k_ctx.dim() != 4 or v_ctx.shape != k_ctx.shape:
+        raise ValueError("k_ctx / v_ctx must both be [L,H,n_c,d]")
+    L, H, n_c, d = k_ctx.shape
+    total, n_src = idx.numel(), src_idx.numel()
+    if offsets.numel() != L * H + 1 or src_offsets.numel() != total + 1:
+        raise ValueError("offsets must hold L*H+1 and src_offsets total+1 entries")
+    dev = k_ctx.device
+    k_out = torch.empty((total, d), dtype=torch.bfloat16, device=dev) if k_out is None else k_out
+    v_out = torch.empty((total, d), dtype=torch.bfloat16, device=dev) if v_out is None else v_out
+    gate = torch.empty(n_src, dtype=torch.float32, device=dev) if gate is None else gate
+    mass = torch.empty(total, dtype=torch.float32, device=dev) if mass is None else mass
+    for t, name, dt, n in ((k_out, "k_out", torch.bfloat16, total * d),
+                           (v_out, "v_out", torch.bfloat16, total * d),
+                           (gate, "gate", torch.float32, n_src),
+                           (mass, "mass", torch.float32, total)):
+        _dev(t, dt, name)
+        if t.numel() < n:
+            raise ValueError(f"{name} too small")
+    _check("kv_merge_compact", _lib.load().kv_merge_compact(
+        _ptr(k_ctx), _ptr(v_ctx), _ptr(offsets), _ptr(idx), _ptr(src_offsets), _ptr(src_idx),
+        _ptr(k_out), _ptr(v_out), _ptr(gate), _ptr(mass), L, H, d, n_c, total, n_src,
+        _stream(stream)))
+    return k_out, v_out, gate, mass
+
+
 # ---------------------------------------------------------------------------
 # attention-free token score (EpiKV page, section 3.2)
 # ---------------------------------------------------------------------------

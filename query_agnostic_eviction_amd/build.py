@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 
 SOURCES = ["kvscore_lse.hip", "kvscore_colmax.hip", "kv_topk.hip",
-           "kv_compact.hip", "epikv.hip", "kvq_api.hip"]
+           "kv_compact.hip", "epikv.hip", "selkv_merge.hip",
+           "kvq_api.hip"]
 
 # per-source extra flags: pass 2 reduces with max3 on finite values and -inf
 # padding only, so NaN semantics (and their canonicalising copies) are off

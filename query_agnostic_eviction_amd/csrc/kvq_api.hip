@@ -342,4 +342,28 @@ int kv_compact_tokens(const void* k_cache, const void* v_cache, const int32_t* i
       (int64_t)L * H * k, k, static_cast<hipStream_t>(stream)));
 }
 
+int kv_merge_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
+                     const int32_t* idx, const int64_t* src_offsets, const int32_t* src_idx,
+                     void* k_out, void* v_out, float* gate, float* mass, int L, int H, int d,
+                     int64_t n_c, int64_t total, int64_t n_src, void* stream) {
+  if (!k_ctx || !v_ctx || !offsets || !idx || !src_offsets || !k_out || !v_out)
+    return KV_ERR_INVALID_ARG;
+  if (n_src > 0 && !src_idx) return KV_ERR_INVALID_ARG;
+  if (L < 1 || H < 1 || n_c < 1 || total < 0 || n_src < 0) return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31 || n_c >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  if (total > (int64_t)L * H * n_c) return KV_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
+  if (!aligned(k_ctx, 16) || !aligned(v_ctx, 16) || !aligned(k_out, 16) ||
+      !aligned(v_out, 16) || !aligned(offsets, 8) || !aligned(idx, 4) ||
+      !aligned(src_offsets, 8) || !aligned(src_idx, 4) || !aligned(gate, 4) ||
+      !aligned(mass, 4))
+    return KV_ERR_ALIGNMENT;
+  if (total == 0) return KV_OK;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_merge(
+      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), offsets, idx,
+      src_offsets, src_idx, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out), gate,
+      mass, L * H, d, n_c, total, n_src, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -85,6 +85,12 @@ hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
 hipError_t launch_select_tokens_grid(const float* scores, long long n, long long k,
                                      int32_t* idx, void* workspace, hipStream_t stream);
 
+// Gated merge of routed tokens into kept rows (SelKV soft cosine gate).
+hipError_t launch_merge(const uint16_t* k_ctx, const uint16_t* v_ctx, const int64_t* offsets,
+                        const int32_t* idx, const int64_t* src_offsets, const int32_t* src_idx,
+                        uint16_t* k_out, uint16_t* v_out, float* gate, float* mass, int LH,
+                        int d, int64_t n_c, int64_t total, int64_t n_src, hipStream_t stream);
+
 // EpiKV token score: hidden-state change norms, then band statistics.
 hipError_t launch_epi_deltas(const uint16_t* h, int n_layers, int64_t n, int D, float* g,
                              hipStream_t stream);

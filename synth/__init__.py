@@ -11,3 +11,4 @@ from .generate import (bf16_bits_to_f32, chunk_rows, default_workers,
                        generate_workload)
 from .epikv import (EPI_ALL, EPI_BY_NAME, EPIKV_R1_8B_64K, EPIKV_TINY, EpiWorkload,
                     generate_hidden, generate_hidden_layer, generate_kv)
+from .routing import nearest_position_routes

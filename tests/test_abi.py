@@ -262,3 +262,22 @@ def test_epikv_validation(lib):
     assert c(P, P, P, P4, P, 2, 2, 128, 100, 10, NUL) == ALN
     assert c(P, P, P2, P, P, 2, 2, 128, 100, 10, NUL) == ALN
     assert c(P, P, P, P, P, 2, 2, 128, 100, 0, NUL) == OK      # nothing to copy, no launch
+
+
+def test_merge_validation(lib):
+    f = lib.kv_merge_compact
+
+    def call(kc=P, vc=P, off=P, idx=P, so=P, si=P, ko=P, vo=P, g=P, m=P, L=2, H=2, d=128,
+             n_c=100, total=50, n_src=30):
+        return f(kc, vc, off, idx, so, si, ko, vo, g, m, L, H, d, n_c, total, n_src, NUL)
+    for name in ("kc", "vc", "off", "idx", "so", "ko", "vo"):
+        assert call(**{name: NUL}) == INV
+    assert call(si=NUL) == INV
+    assert call(si=NUL, n_src=0, total=0) == OK          # nothing to do, no launch
+    assert call(g=NUL, m=NUL, total=0) == OK
+    assert call(total=401) == INV
+    assert call(n_src=-1) == INV
+    assert call(d=96) == UNS
+    assert call(so=P4) == ALN
+    assert call(g=P2) == ALN
+    assert call(ko=P4) == ALN

@@ -1,0 +1,176 @@
+"""GPU parity of the gated merge (SelKV page, section 1: soft cosine gate)
+through libkvq's C ABI against oracle.selkv.
+
+Tolerances: gates within 2e-6 absolute (fp32 dot products of at most 4
+terms per lane plus a 6-level butterfly, against float64); merged rows
+within half a bf16 ulp of the float64 value plus the fp32 accumulation
+error (2e-6 of the largest magnitude in the row's group); an empty routing
+list reproduces kv_compact bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import query_agnostic_eviction_amd as kvq
+from oracle import selkv as S
+from parity_util import dev_bf16_bits, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+GATE_ATOL = 2e-6
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    kvq.api._lib.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a).astype(dtype)).cuda()
+
+
+def check_merge(k_bits, v_bits, off, idx, so, si, got, rows=None):
+    """got = (k_out, v_out, gate, mass) from the GPU; compare rows (default all)."""
+    K, V = oracle.bf16_to_f64(k_bits), oracle.bf16_to_f64(v_bits)
+    rk, rv, rg, rm = S.merge_compact(K, V, off, idx, so, si)
+    ko = synth.bf16_bits_to_f32(dev_bf16_bits(got[0])).astype(np.float64)
+    vo = synth.bf16_bits_to_f32(dev_bf16_bits(got[1])).astype(np.float64)
+    g, m = got[2].cpu().numpy(), got[3].cpu().numpy()
+    assert np.all(np.abs(g - rg) <= GATE_ATOL), np.abs(g - rg).max()
+    cnt = np.diff(so)
+    assert np.all(np.abs(m - rm) <= GATE_ATOL * (1 + cnt))
+    H = K.shape[1]
+    rows = range(int(off[-1])) if rows is None else rows
+    for t in rows:
+        lh = int(np.searchsorted(off, t, side="right") - 1)
+        l, h = divmod(lh, H)
+        group = [idx[t]] + [j for j in si[so[t]:so[t + 1]] if 0 <= j < K.shape[2]]
+        M = max(np.abs(K[l, h, group]).max(), np.abs(V[l, h, group]).max())
+        for out, ref in ((ko[t], rk[t]), (vo[t], rv[t])):
+            tol = 2.0 ** -8 * np.abs(ref) + 2e-6 * M
+            assert np.all(np.abs(out - ref) <= tol), (t, np.abs(out - ref).max())
+
+
+def _case(L, H, n_c, d, r, seed, scale_pairs=False):
+    rng = np.random.default_rng(seed)
+    kb = synth.f64_to_bf16_bits(rng.normal(size=(L, H, n_c, d)))
+    vv = rng.normal(size=(L, H, n_c, d))
+    if scale_pairs:
+        # neighbours with parallel, opposite and zero values: gates 1, 0, 0
+        vv[:, :, 1::4] = 2.0 * vv[:, :, 0::4][:, :, :vv[:, :, 1::4].shape[2]]
+        vv[:, :, 2::4] = -vv[:, :, 0::4][:, :, :vv[:, :, 2::4].shape[2]]
+        vv[:, :, 3::7] = 0.0
+    vb = synth.f64_to_bf16_bits(vv)
+    s = rng.random((L, H, n_c)).astype(np.float32)
+    off, idx = oracle.select(s, r, 0)
+    so, si = synth.nearest_position_routes(off, idx, n_c)
+    return kb, vb, off, idx, so, si
+
+
+@pytest.mark.parametrize("L,H,n_c,d,r,seed,pairs", [
+    (1, 1, 7, 64, 0.3, 0, False), (2, 3, 300, 128, 0.25, 1, False),
+    (1, 2, 1000, 256, 0.1, 2, True), (2, 2, 513, 128, 0.5, 3, True),
+    (1, 1, 64, 64, 1.0, 4, False)])
+def test_merge_parity(L, H, n_c, d, r, seed, pairs):
+    _say("case: merge", L, H, n_c, d, r)
+    kb, vb, off, idx, so, si = _case(L, H, n_c, d, r, seed, pairs)
+    got = kvq.kv_merge_compact(to_dev_bf16(kb), to_dev_bf16(vb), _dev(off, np.int64),
+                               _dev(idx, np.int32), _dev(so, np.int64), _dev(si, np.int32))
+    torch.cuda.synchronize()
+    check_merge(kb, vb, off, idx, so, si, got)
+
+
+def test_empty_routes_equal_compaction():
+    kb, vb, off, idx, so, si = _case(2, 2, 400, 128, 0.3, 5)
+    so0 = np.zeros_like(so)
+    kd, vd = to_dev_bf16(kb), to_dev_bf16(vb)
+    offd, idxd = _dev(off, np.int64), _dev(idx, np.int32)
+    ko, vo, g, m = kvq.kv_merge_compact(kd, vd, offd, idxd, _dev(so0, np.int64),
+                                        torch.zeros(1, dtype=torch.int32, device="cuda")[:0])
+    kc, vc = kvq.kv_compact(kd, vd, offd, idxd)
+    assert torch.equal(ko.view(torch.int16), kc.view(torch.int16))
+    assert torch.equal(vo.view(torch.int16), vc.view(torch.int16))
+    assert torch.all(m == 0)
+
+
+def test_invalid_sources_and_rows():
+    kb, vb, off, idx, so, si = _case(1, 2, 200, 64, 0.2, 6)
+    si = si.copy()
+    si[::5] = -1
+    si[1::9] = 200
+    idx = idx.copy()
+    idx[3] = 999                       # an invalid kept index: zero row, no merge
+    got = kvq.kv_merge_compact(to_dev_bf16(kb), to_dev_bf16(vb), _dev(off, np.int64),
+                               _dev(idx, np.int32), _dev(so, np.int64), _dev(si, np.int32))
+    torch.cuda.synchronize()
+    assert np.all(dev_bf16_bits(got[0])[3] == 0) and np.all(dev_bf16_bits(got[1])[3] == 0)
+    g = got[2].cpu().numpy()
+    assert np.all(g[so[3]:so[4]] == 0) and got[3][3].item() == 0.0
+    bad = (si < 0) | (si >= 200)
+    assert np.all(g[bad] == 0)
+    # the oracle (which takes valid kept sets only) on the same sources with a
+    # valid index in row 3; row 3's own gates were checked above
+    idx_ok = idx.copy()
+    idx_ok[3] = 0
+    K, V = oracle.bf16_to_f64(kb), oracle.bf16_to_f64(vb)
+    rk, rv, rg, rm = S.merge_compact(K, V, off, idx_ok, so, si)
+    keep = np.ones(g.size, bool)
+    keep[so[3]:so[4]] = False
+    assert np.all(np.abs(g[keep] - rg[keep]) <= GATE_ATOL)
+
+
+def test_deterministic():
+    kb, vb, off, idx, so, si = _case(2, 2, 2000, 128, 0.3, 7)
+    args = (to_dev_bf16(kb), to_dev_bf16(vb), _dev(off, np.int64), _dev(idx, np.int32),
+            _dev(so, np.int64), _dev(si, np.int32))
+    a = kvq.kv_merge_compact(*args)
+    b = kvq.kv_merge_compact(*args)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+def test_llama8b_8k_full_size_sampled_heads():
+    # the full 32 x 8 x 8192 x 128 cache, kept sets of the r = 0.3 budget and
+    # nearest-position routing; the oracle checks three whole heads
+    w = synth.LLAMA8B_8K
+    _say("case: merge full", w.name)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    shape = (w.L, w.H, w.n_c, w.d)
+    kd = (torch.randn(shape, device="cuda", generator=gen)).to(torch.bfloat16)
+    vd = (torch.randn(shape, device="cuda", generator=gen)).to(torch.bfloat16)
+    rng = np.random.default_rng(12)
+    s = rng.random((w.L, w.H, w.n_c)).astype(np.float32)
+    off, idx = oracle.select(s, w.keep_ratio, 0)
+    so, si = synth.nearest_position_routes(off, idx, w.n_c)
+    got = kvq.kv_merge_compact(kd, vd, _dev(off, np.int64), _dev(idx, np.int32),
+                               _dev(so, np.int64), _dev(si, np.int32))
+    torch.cuda.synchronize()
+    for (l, h) in [(0, 0), (w.L - 1, w.H - 1), (17, 3)]:
+        lh = l * w.H + h
+        a, b = int(off[lh]), int(off[lh + 1])
+        kb = dev_bf16_bits(kd[l, h])[None, None]
+        vb = dev_bf16_bits(vd[l, h])[None, None]
+        so_h = so[a:b + 1] - so[a]
+        si_h = si[so[a]:so[b]]
+        sub = (got[0][a:b], got[1][a:b], got[2][int(so[a]):int(so[b])], got[3][a:b])
+        check_merge(kb, vb, np.array([0, b - a]), idx[a:b], so_h, si_h, sub)
+
+
+def test_many_heads_global_search():
+    # more heads than the LDS-staged offsets hold: the head search runs on
+    # the offsets in global memory
+    kb, vb, off, idx, so, si = _case(40, 16, 24, 64, 0.3, 8)
+    got = kvq.kv_merge_compact(to_dev_bf16(kb), to_dev_bf16(vb), _dev(off, np.int64),
+                               _dev(idx, np.int32), _dev(so, np.int64), _dev(si, np.int32))
+    torch.cuda.synchronize()
+    check_merge(kb, vb, off, idx, so, si, got)

@@ -98,3 +98,25 @@ def test_generate_workload_matches_heads():
             d = synth.generate_head(w, l, h)
             for k in d:
                 assert np.array_equal(full[k][l, h], d[k])
+
+
+def test_nearest_position_routes():
+    off = np.array([0, 2, 3])
+    idx = np.array([1, 5, 3])
+    so, si = synth.nearest_position_routes(off, idx, 8)
+    assert so.tolist() == [0, 3, 6, 13]
+    assert si.tolist() == [0, 2, 3, 4, 6, 7, 0, 1, 2, 4, 5, 6, 7]
+    # every evicted position routed exactly once, to its nearest kept one
+    rng = np.random.default_rng(0)
+    n_c = 500
+    kept = [np.sort(rng.choice(n_c, size=s, replace=False)) for s in (1, 50, 499)]
+    off = np.concatenate([[0], np.cumsum([k.size for k in kept])])
+    idx = np.concatenate(kept)
+    so, si = synth.nearest_position_routes(off, idx, n_c)
+    for h, k in enumerate(kept):
+        rows = range(off[h], off[h + 1])
+        got = np.concatenate([si[so[t]:so[t + 1]] for t in rows])
+        assert sorted(got.tolist()) == sorted(set(range(n_c)) - set(k.tolist()))
+        for t in rows:
+            for j in si[so[t]:so[t + 1]]:
+                assert abs(j - idx[t]) == np.abs(k - j).min()
