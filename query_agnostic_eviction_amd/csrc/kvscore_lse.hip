@@ -21,6 +21,8 @@
 //  * exp is taken as exp2 with the scale folded into one FMA per logit; the
 //    running max is updated lazily (see accumulate2), so the hot path has no
 //    per-logit max, and masked keys enter as a -inf accumulator seed.
+//  * Subtile sums enter each lane's running sum with Kahan compensation
+//    (per subtile, not per logit), so 128K-key rows stay at fp32 accuracy.
 //  * The loop is software-pipelined by one 32-key subtile so the matrix
 //    cores and the VALU/transcendental units work at the same time.
 #include "kvq_device.h"
@@ -130,7 +132,10 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
   // rounding while the hot path costs one FMA, one exp2 and one add per logit.
   float m[2] = {kNegBig, kNegBig};
   float nmc[2] = {-kNegBig * c2, -kNegBig * c2};
-  float sum[2] = {0.f, 0.f};
+  // running sums with a compensation term (Kahan): long contexts add
+  // thousands of subtile sums of similar size, whose rounding errors would
+  // otherwise accumulate
+  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
 
   auto accumulate2 = [&](const f32x16& x0, const f32x16& x1) {
@@ -160,7 +165,9 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
 #pragma unroll
         for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
         const float mn = __builtin_fmaxf(m[f], tm);
-        sum[f] *= fast_exp2((m[f] - mn) * c2);
+        const float rescale = fast_exp2((m[f] - mn) * c2);
+        sum[f] *= rescale;
+        comp[f] *= rescale;
         m[f] = mn;
         nmc[f] = -mn * c2;
         float t = 0.f;
@@ -169,8 +176,14 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
         *tsp[f] = t;
       }
     }
-    sum[0] += ts0;
-    sum[1] += ts1;
+    const float ts[2] = {ts0, ts1};
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const float y = ts[f] - comp[f];
+      const float t = sum[f] + y;
+      comp[f] = (t - sum[f]) - y;
+      sum[f] = t;
+    }
   };
 
   // Accumulator seed: 0 for keys a row sees, -inf for keys it must not see
@@ -249,10 +262,11 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
   // merge the two half-waves that hold the same query, then store
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
+    const float own = sum[f] - comp[f];
     const float mo = __shfl_xor(m[f], 32);
-    const float so = __shfl_xor(sum[f], 32);
+    const float so = __shfl_xor(own, 32);
     const float M = __builtin_fmaxf(m[f], mo);
-    const float S = sum[f] * fast_exp2((m[f] - M) * c2) + so * fast_exp2((mo - M) * c2);
+    const float S = own * fast_exp2((m[f] - M) * c2) + so * fast_exp2((mo - M) * c2);
     const float val = __builtin_fmaf(M, scale, __logf(S));
     const int pos = fpos0[f] + (lane & 31);
     if (lane < 32 && fvalid[f] && pos < n_in)

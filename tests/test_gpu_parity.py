@@ -5,6 +5,8 @@ and compaction bit-exact; top-k on GPU scores exact outside the near-tie band.
 Definitions: KVzip page ("KVzip: Query-Agnostic KV Cache Compression with
 Context Reconstruction"), section 3.2 (score), section 4.1 (budget).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -432,12 +434,28 @@ def _model_budget_checks(w, dev, sc, heads, S_ref):
                          f"head score ({l},{h})")
 
 
+GOLDEN_128K = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "llama3.1-8b-128k_head31-7.npz")
+
+
 def test_llama8b_128k_full_size_sampled():
     w = synth.LLAMA8B_128K
     l, h = 0, 0
+    gl, gh_ = w.L - 1, w.H - 1      # the head stored by tests/golden/make_llama128k_head.py
     _say("case: full", w.name)
-    dev, gens = _full_size_inputs(w, [(l, h)])
+    dev, gens = _full_size_inputs(w, [(l, h), (gl, gh_)])
     out = _run(w, dev)
+    # whole-head parity against the float64 oracle's stored values
+    gold = np.load(GOLDEN_128K)
+    assert (int(gold["layer"]), int(gold["head"])) == (gl, gh_)
+    S_gold = gold["scores"].astype(np.float64)
+    check_scores(out["scores"][gl, gh_].cpu().numpy(), S_gold, f"scores[{gl},{gh_}]")
+    check_lse(out["lse"][gl, gh_].cpu().numpy()[:, ::16], gold["lse_rows16"].astype(np.float64),
+              f"lse[{gl},{gh_}] every 16th row")
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    band = check_topk_band(head_kept(out["offsets"].cpu().numpy(), out["idx"].cpu().numpy(),
+                                     gl * w.H + gh_), S_gold, k)
+    _say(f"head ({gl},{gh_}): whole head within tolerance, near-tie band holds {band} keys")
     gh = gens[(l, h)]
     q, kc, kn = oracle.workload_head_inputs(gh)
     lse_g = out["lse"][l, h].cpu().numpy()
