@@ -20,7 +20,7 @@
 namespace kvq {
 namespace {
 
-constexpr int kRun = 64;    // consecutive rows per workgroup
+constexpr int kRun = 16;    // consecutive rows per workgroup
 constexpr int kGroup = 4;   // rows loaded together (loads in flight per thread)
 
 __device__ __forceinline__ float sq_diff_sum(u32x4 a, u32x4 b, float acc) {
