@@ -11,7 +11,8 @@
 //
 // Mapping on gfx950:
 //  * A workgroup of 4 waves owns 384 cached keys (3 fragments of 32 per
-//    wave, kept in registers as the B operand); it sweeps all G * n_in query
+//    wave, kept in registers as the B operand; 256 keys in 2 fragments at
+//    d = 256, so that two waves fit per SIMD); it sweeps all G * n_in query
 //    rows of its head in 32 KB tiles (16384 / d rows), double-buffered and
 //    filled by LDS-DMA straight from HBM together with the rows' lse.
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
@@ -34,15 +35,14 @@ struct ColCfg {
   static constexpr int NSUB = QT / 32;
   static constexpr int KS = D / 16;
   static constexpr int LSE_LOADS = QT / 64;  // 4-byte DMA instructions per tile
+  // cached-key fragments of 32 per wave: each operand read from LDS feeds NF
+  // matrix ops; at d = 256 two, so that two waves fit per SIMD
+  static constexpr int NF = D == 256 ? 2 : 3;
+  static constexpr int KEYS_PER_WG = 4 * NF * 32;
 };
 
-// cached-key fragments of 32 per wave: each operand read from LDS feeds NF
-// matrix ops; 4 waves x NF x 32 keys per workgroup
-constexpr int NF = 3;
-constexpr int kKeysPerWg = 4 * NF * 32;
-
 template <int D>
-__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
+__global__ __launch_bounds__(256, 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const float* __restrict__ lse, float* __restrict__ scores,
     const ScoreShape sh, int wg_per_head, float c2, float inv_scale) {
@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void colmax_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int u = logical / wg_per_head;  // work item: (layer, KV head[, chunk])
-  const int j0 = (logical % wg_per_head) * kKeysPerWg;
+  constexpr int NF = C::NF;
+  const int j0 = (logical % wg_per_head) * C::KEYS_PER_WG;
 
   // this wave's two key fragments -> registers (B operand layout)
   bf16x8 bk[NF][C::KS];
@@ -190,7 +191,7 @@ template <int D>
 hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
                            const float* lse, float* scores, const ScoreShape& s,
                            hipStream_t stream) {
-  const int wg_per_head = (s.n_c + kKeysPerWg - 1) / kKeysPerWg;
+  const int wg_per_head = (s.n_c + ColCfg<D>::KEYS_PER_WG - 1) / ColCfg<D>::KEYS_PER_WG;
   const long long grid = (long long)s.nheads * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;

@@ -6,10 +6,11 @@
 // lse[l][h][g][i] = ln sum_{seen j} exp(scale * <q_{g,i}, k_j>).
 //
 // Mapping on gfx950:
-//  * A workgroup of 4 waves owns 8 query fragments of 32 rows each (a
-//    fragment is 32 consecutive positions of one query head g; fragments of a
-//    head are numbered b * G + g over 32-position blocks b).  Each wave keeps
-//    its two fragments' queries in registers for the whole key sweep.
+//  * A workgroup of 4 waves owns 8 query fragments of 32 rows each (4 at
+//    d = 256; a fragment is 32 consecutive positions of one query head g;
+//    fragments of a head are numbered b * G + g over 32-position blocks b).
+//    Each wave keeps its two fragments' queries (one at d = 256, so that two
+//    waves fit per SIMD) in registers for the whole key sweep.
 //  * Keys stream through LDS in 32 KB tiles (16384 / d keys), double-buffered
 //    and filled by LDS-DMA straight from HBM while the previous tile is in
 //    use: first the cached keys, then the new keys up to the workgroup's last
@@ -19,7 +20,7 @@
 //    the softmax sums stay lane-local; the two half-waves that share a query
 //    merge once at the end.
 //  * exp is taken as exp2 with the scale folded into one FMA per logit; the
-//    running max is updated lazily (see accumulate2), so the hot path has no
+//    running max is updated lazily (see accumulate), so the hot path has no
 //    per-logit max, and masked keys enter as a -inf accumulator seed.
 //  * Subtile sums enter each lane's running sum with Kahan compensation
 //    (per subtile, not per logit), so 128K-key rows stay at fp32 accuracy.
@@ -38,10 +39,14 @@ struct LseCfg {
   static constexpr int KT = Tile<D>::ROWS;  // keys per tile
   static constexpr int NSUB = KT / 32;      // 32-key subtiles per tile
   static constexpr int KS = D / 16;         // k-steps of the 32x32x16 op
+  // query fragments per wave: two share each key operand read, but at
+  // d = 256 their registers would leave one wave per SIMD, so one
+  static constexpr int NFQ = D == 256 ? 1 : 2;
+  static constexpr int FPW = 4 * NFQ;      // fragments per workgroup
 };
 
 template <int D>
-__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
+__global__ __launch_bounds__(256, 2) void lse_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const uint16_t* __restrict__ k_new, float* __restrict__ lse,
     const ScoreShape sh, int nfrag_head, int wg_per_head, float c2) {
@@ -57,26 +62,27 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
   // latest positions (most keys) first
   const int wgi = wg_per_head - 1 - logical % wg_per_head;
 
+  constexpr int NFQ = C::NFQ;
   // fragment bookkeeping (uniform per wave)
-  const int F_first = 8 * wgi;
-  const int F_last = min(8 * wgi + 7, nfrag_head - 1);
+  const int F_first = C::FPW * wgi;
+  const int F_last = min(C::FPW * wgi + C::FPW - 1, nfrag_head - 1);
   const int pos_min = 32 * (F_first / G);
   const int new_len = min(n_in, 32 * (F_last / G + 1));
 
-  int fg[2], fpos0[2];
-  bool fvalid[2];
+  int fg[NFQ], fpos0[NFQ];
+  bool fvalid[NFQ];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int F = 8 * wgi + 2 * wave + f;
+  for (int f = 0; f < NFQ; ++f) {
+    const int F = C::FPW * wgi + NFQ * wave + f;
     fvalid[f] = F < nfrag_head;
     fg[f] = fvalid[f] ? F % G : 0;
     fpos0[f] = fvalid[f] ? 32 * (F / G) : 0;
   }
 
-  // queries of both fragments -> registers (B operand layout)
-  bf16x8 bq[2][C::KS];
+  // queries of the wave's fragments -> registers (B operand layout)
+  bf16x8 bq[NFQ][C::KS];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NFQ; ++f) {
     const int pos = fpos0[f] + (lane & 31);
     const bool ok = fvalid[f] && pos < n_in;
     const uint16_t* src = q + map_offset(sh.q, u, sh.inner) +
@@ -130,40 +136,45 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
   // stay far from overflow (< 2^64 per subtile) and terms far below m only
   // underflow where they are negligible, so the result is exact to fp32
   // rounding while the hot path costs one FMA, one exp2 and one add per logit.
-  float m[2] = {kNegBig, kNegBig};
-  float nmc[2] = {-kNegBig * c2, -kNegBig * c2};
+  float m[NFQ], nmc[NFQ];
   // running sums with a compensation term (Kahan): long contexts add
   // thousands of subtile sums of similar size, whose rounding errors would
   // otherwise accumulate
-  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
+  float sum[NFQ], comp[NFQ];
+#pragma unroll
+  for (int f = 0; f < NFQ; ++f) {
+    m[f] = kNegBig;
+    nmc[f] = -kNegBig * c2;
+    sum[f] = comp[f] = 0.f;
+  }
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
 
-  auto accumulate2 = [&](const f32x16& x0, const f32x16& x1) {
+  auto accumulate = [&](const f32x16* x) {
     // four running partial sums per fragment keep few temporaries live
-    float e0[4], e1[4];
+    float e[NFQ][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      e0[a] = fast_exp2(__builtin_fmaf(x0[a], c2, nmc[0]));
-      e1[a] = fast_exp2(__builtin_fmaf(x1[a], c2, nmc[1]));
-    }
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int a = 4; a < 16; ++a) {
-      e0[a & 3] += fast_exp2(__builtin_fmaf(x0[a], c2, nmc[0]));
-      e1[a & 3] += fast_exp2(__builtin_fmaf(x1[a], c2, nmc[1]));
+      for (int f = 0; f < NFQ; ++f) e[f][a] = fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
+#pragma unroll
+    for (int a = 4; a < 16; ++a)
+#pragma unroll
+      for (int f = 0; f < NFQ; ++f) e[f][a & 3] += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
+    float ts[NFQ];
+    bool big = false;
+#pragma unroll
+    for (int f = 0; f < NFQ; ++f) {
+      ts[f] = (e[f][0] + e[f][1]) + (e[f][2] + e[f][3]);
+      big = big || !(ts[f] <= kRescaleAt);
     }
-    float ts0 = (e0[0] + e0[1]) + (e0[2] + e0[3]);
-    float ts1 = (e1[0] + e1[1]) + (e1[2] + e1[3]);
-    if (!(ts0 <= kRescaleAt) || !(ts1 <= kRescaleAt)) {
+    if (big) {
       // rare path: raise the running max to this subtile's max and re-sum
-      const f32x16* xs[2] = {&x0, &x1};
-      float* tsp[2] = {&ts0, &ts1};
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        if (*tsp[f] <= kRescaleAt) continue;
-        const f32x16& x = *xs[f];
-        float tm = x[0];
+      for (int f = 0; f < NFQ; ++f) {
+        if (ts[f] <= kRescaleAt) continue;
+        float tm = x[f][0];
 #pragma unroll
-        for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
+        for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[f][a]);
         const float mn = __builtin_fmaxf(m[f], tm);
         const float rescale = fast_exp2((m[f] - mn) * c2);
         sum[f] *= rescale;
@@ -172,13 +183,12 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
         nmc[f] = -mn * c2;
         float t = 0.f;
 #pragma unroll
-        for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc[f]));
-        *tsp[f] = t;
+        for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
+        ts[f] = t;
       }
     }
-    const float ts[2] = {ts0, ts1};
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < NFQ; ++f) {
       const float y = ts[f] - comp[f];
       const float t = sum[f] + y;
       comp[f] = (t - sum[f]) - y;
@@ -201,30 +211,33 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
 
   // software pipeline: the MFMAs of one 32-key subtile run while the VALU
   // reduces the previous subtile's logits
-  f32x16 p0, p1;
+  f32x16 p[NFQ];
 #pragma unroll
-  for (int a = 0; a < 16; ++a) p0[a] = p1[a] = -__builtin_inff();
+  for (int f = 0; f < NFQ; ++f)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) p[f][a] = -__builtin_inff();
 
   // one 32-key subtile; unmasked subtiles start the chain from an inline zero
   auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase) {
-    f32x16 c0, c1;
-    if (masked) {
-      c0 = seed(0, seg, kbase);
-      c1 = seed(1, seg, kbase);
-    } else {
-      const f32x16 z = {};
-      c0 = z;
-      c1 = z;
+    f32x16 c[NFQ];
+#pragma unroll
+    for (int f = 0; f < NFQ; ++f) {
+      if (masked) {
+        c[f] = seed(f, seg, kbase);
+      } else {
+        const f32x16 z = {};
+        c[f] = z;
+      }
     }
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
-      c0 = mfma32(a, bq[0][s], c0);
-      c1 = mfma32(a, bq[1][s], c1);
+#pragma unroll
+      for (int f = 0; f < NFQ; ++f) c[f] = mfma32(a, bq[f][s], c[f]);
     }
-    accumulate2(p0, p1);
-    p0 = c0;
-    p1 = c1;
+    accumulate(p);
+#pragma unroll
+    for (int f = 0; f < NFQ; ++f) p[f] = c[f];
   };
 
   // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
@@ -257,11 +270,11 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void lse_kernel(
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
-  accumulate2(p0, p1);
+  accumulate(p);
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NFQ; ++f) {
     const float own = sum[f] - comp[f];
     const float mo = __shfl_xor(m[f], 32);
     const float so = __shfl_xor(own, 32);
@@ -280,7 +293,7 @@ hipError_t launch_lse_d(const uint16_t* q, const uint16_t* k_ctx,
                         hipStream_t stream) {
   const int nb = (s.n_in + 31) / 32;
   const int nfrag = s.G * nb;
-  const int wg_per_head = (nfrag + 7) / 8;
+  const int wg_per_head = (nfrag + LseCfg<D>::FPW - 1) / LseCfg<D>::FPW;
   const long long grid = (long long)s.nheads * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
