@@ -86,6 +86,17 @@ def recorded_traffic(kernel: str, workload: str):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def calibration_copy(torch):
     """A plain 1 GiB device-to-device copy, run once untimed and once timed:
     its bytes read + written per second are the practical HBM ceiling of a
@@ -100,6 +111,24 @@ def calibration_copy(torch):
     e1.record()
     torch.cuda.synchronize()
     return 2.0 * CALIB_BYTES / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cold_time_ms(torch, fn, reps=5):
+    """Median time of fn() on the current stream, each run preceded by a
+    1 GiB write to a scratch buffer so that no input is left in the 256 MB
+    last-level cache (MALL) when fn starts."""
+    scratch = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for r in range(reps):
+        scratch.fill_(float(r))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(times))
 
 
 def synth_total(w, mode):
@@ -151,6 +180,9 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None, merge=False):
         "sample": f"{len(heads)} whole (layer, KV head) slices of {w.name} "
                   f"({done} context KV pairs): float64 attention rows, max score, "
                   f"top-k and {'gated merge' if merge else 'gather'}; {t_oracle:.1f} s",
+        "cpu_model": cpu_model(),
+        # every head costs the same, so the whole workload would take this long
+        "extrapolated_full_s": round(t_oracle / len(heads) * w.L * w.H, 1),
     }
 
 
@@ -164,6 +196,10 @@ def main():
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunked scoring with this chunk length (0 = whole context)")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="fill the inputs with seeded N(0,1) values made on the GPU instead of "
+                         "the host generator (for timing the largest workloads; the kernels' "
+                         "time does not depend on the values)")
     ap.add_argument("--merge", action="store_true",
                     help="gated merge (soft cosine gate) of the evicted tokens into their "
                          "nearest kept position instead of plain compaction")
@@ -186,7 +222,10 @@ def main():
 
     # host work first: input generation and the oracle baseline (thread pools)
     t0 = time.perf_counter()
-    if chunk:
+    gen = None
+    if args.device_inputs:
+        pass
+    elif chunk:
         gen = synth.generate_chunked_workload(w, chunk, workers=min(16, synth.default_workers()))
     else:
         gen = synth.generate_workload(w, workers=min(16, synth.default_workers()))
@@ -201,9 +240,23 @@ def main():
     import query_agnostic_eviction_amd as kvq
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
-           for k, v in gen.items()}
-    del gen
+    if gen is not None:
+        dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+               for k, v in gen.items()}
+        del gen
+    else:
+        rows = synth.chunk_rows(w, chunk) if chunk else w.n_in
+        shapes = {"q": (w.L, w.H, rows * w.G, w.d) if chunk else (w.L, w.H, w.G, w.n_in, w.d),
+                  "k_ctx": (w.L, w.H, w.n_c, w.d), "k_new": (w.L, w.H, rows, w.d),
+                  "v_ctx": (w.L, w.H, w.n_c, w.d)}
+        rng = torch.Generator(device="cuda").manual_seed(w.seed)
+        dev = {}
+        for k, shp in shapes.items():
+            t = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+            for l in range(w.L):   # per layer: bounded fp32 temporaries
+                t[l] = torch.randn(shp[1:], generator=rng, device="cuda").to(torch.bfloat16)
+            dev[k] = t
+        torch.cuda.synchronize()
     L, H, G, n_c, n_in, d = w.L, w.H, w.G, w.n_c, w.n_in, w.d
     scale = float(w.scale)
     total = work["kept_rows"]
@@ -284,6 +337,15 @@ def main():
     # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the counters
     copy_gbs = calibration_copy(torch)
 
+    # compaction alone with no input left in the last-level cache
+    def compact_only():
+        if route:
+            kvq.kv_merge_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, route["so"],
+                                 route["si"], k_out, v_out, gate, mass, stream)
+        else:
+            kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, k_out, v_out, stream)
+    cold_ms = cold_time_ms(torch, compact_only)
+
     ms_per_step = 1e3 * elapsed / args.steps
     value = w.context_pairs / (elapsed / args.steps)
     lse_tf = work["lse_flops"] / (ms["kvscore_lse"] * 1e-3) / 1e12
@@ -324,7 +386,8 @@ def main():
         "config": {"workload": w.name, "L": L, "H": H, "G": G, "d": d, "n_c": n_c,
                    "n_prompt": w.n_prompt, "keep_ratio": w.keep_ratio,
                    "select_mode": args.mode, "chunk": chunk,
-                   "merge": "soft cosine gate, nearest kept position" if args.merge else None},
+                   "merge": "soft cosine gate, nearest kept position" if args.merge else None,
+                   "inputs": "device N(0,1)" if args.device_inputs else "synth generator"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v, 4) for n, v in ms.items()},
@@ -332,6 +395,8 @@ def main():
         "lse_mfma_frac": round(lse_tf / PEAK_BF16_TFLOPS, 4),
         "colmax_mfma_frac": round(col_tf / PEAK_BF16_TFLOPS, 4),
         "compact_hbm_frac": round(cmp_gbs / PEAK_HBM_GBS, 4),
+        "compact_cold_hbm_frac": round(work["merge_bytes" if args.merge else "compact_bytes"]
+                                       / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gbs": round(sel_gbs, 1),
         "copy_gbs": round(copy_gbs, 1),
     }
@@ -389,6 +454,9 @@ def epikv_cpu_baseline(w, hidden, seconds):
         "sample": f"first {N} of {w.n} tokens of {w.name}: float64 deltas of "
                   f"{hidden.shape[0]} hidden layers, rolling z-scores, top-{k}, gather of "
                   f"{w.L}x{w.H} heads; {t:.1f} s",
+        "cpu_model": cpu_model(),
+        # work is linear in the trace length
+        "extrapolated_full_s": round(t * w.n / N, 1),
     }
 
 
@@ -457,6 +525,9 @@ def run_epikv(args):
                             for s in range(args.steps)]))
           for i, n in enumerate(names)}
     copy_gbs = calibration_copy(torch)
+    cold = {"kv_epi_deltas": cold_time_ms(torch, lambda: kvq.kv_epi_deltas(h, g, stream)),
+            "kv_compact_tokens": cold_time_ms(
+                torch, lambda: kvq.kv_compact_tokens(kc, vc, idx, k_out, v_out, stream))}
 
     key = {"kv_epi_deltas": "deltas_bytes", "kv_epi_scores": "scores_bytes",
            "kv_select_tokens": "select_bytes", "kv_compact_tokens": "compact_bytes"}
@@ -486,6 +557,8 @@ def run_epikv(args):
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v, 4) for n, v in ms.items()},
         "hbm_frac": {n: round(gbs[n] / PEAK_HBM_GBS, 4) for n in names},
+        "cold_hbm_frac": {n: round(work[key[n]] / (cold[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                          for n in cold},
         "copy_gbs": round(copy_gbs, 1),
     }
     print(json.dumps(line), flush=True)
