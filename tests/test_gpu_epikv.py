@@ -242,3 +242,19 @@ def test_epikv_r1_8b_64k_full_size():
     for (l, h) in [(0, 0), (w.L - 1, w.H - 1), (13, 5)]:
         assert torch.equal(ko[l, h].view(torch.int16), kc[l, h][idx_dev.long()].view(torch.int16))
         assert torch.equal(vo[l, h].view(torch.int16), vc[l, h][idx_dev.long()].view(torch.int16))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(i):
+    rng = np.random.default_rng(7000 + i)
+    n = int(rng.choice([1, 2, 63, 64, 65, int(rng.integers(2, 5000))]))
+    D = int(8 * rng.integers(1, 1025))
+    n_a, n_b = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    win = int(rng.choice([1, 2, 64, int(rng.integers(1, 1025))]))
+    eps = float(rng.choice([1e-6, 1e-3, 1.0]))
+    w = synth.EPIKV_TINY.shrink(n=n, D=D, window=win, eps=eps, seed=i,
+                                budget=int(rng.integers(1, n + 1)),
+                                band_a=tuple(range(1, 1 + n_a)),
+                                band_b=tuple(range(10, 10 + n_b)))
+    hbits = synth.generate_hidden(w)
+    run_and_check(w, hbits, n_a, bool(rng.integers(2)))

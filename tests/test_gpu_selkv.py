@@ -174,3 +174,21 @@ def test_many_heads_global_search():
                                _dev(idx, np.int32), _dev(so, np.int64), _dev(si, np.int32))
     torch.cuda.synchronize()
     check_merge(kb, vb, off, idx, so, si, got)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_shapes(i):
+    rng = np.random.default_rng(8000 + i)
+    L, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    n_c = int(rng.choice([1, 2, 7, int(rng.integers(1, 1500))]))
+    d = int(rng.choice([64, 128, 256]))
+    r = float(rng.choice([0.01, 0.2, 0.5, 1.0]))
+    mode = int(rng.integers(3))
+    kb, vb, _, _, _, _ = _case(L, H, n_c, d, r, 8100 + i, bool(rng.integers(2)))
+    s = rng.random((L, H, n_c)).astype(np.float32)
+    off, idx = oracle.select(s, r, mode)          # per-head counts vary in modes 1, 2
+    so, si = synth.nearest_position_routes(off, idx, n_c)
+    got = kvq.kv_merge_compact(to_dev_bf16(kb), to_dev_bf16(vb), _dev(off, np.int64),
+                               _dev(idx, np.int32), _dev(so, np.int64), _dev(si, np.int32))
+    torch.cuda.synchronize()
+    check_merge(kb, vb, off, idx, so, si, got)
