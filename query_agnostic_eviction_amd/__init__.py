@@ -12,4 +12,4 @@ from .api import (KvqError, epikv_evict, evict, kv_chunk_layout, kv_compact,
                   kv_select_tokens_workspace_bytes, kv_status_string, kv_topk_select, kv_topk_total,
                   kv_topk_workspace_bytes, kvscore_chunked_colmax,
                   kvscore_chunked_lse, kvscore_colmax, kvscore_lse, score,
-                  score_chunked)
+                  score_chunked, select, compact)

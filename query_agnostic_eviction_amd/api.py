@@ -431,6 +431,16 @@ def score_chunked(q, k_ctx, k_new, G, n_prompt, chunk, scale=None, stream=None):
     return scores, lse
 
 
+def select(scores, keep_ratio, mode=0, stream=None):
+    """(offsets, idx) of the kept pairs (kv_topk_select)."""
+    return kv_topk_select(scores, keep_ratio, mode, stream=stream)
+
+
+def compact(k_ctx, v_ctx, offsets, idx, stream=None):
+    """(k_out, v_out): the kept rows (kv_compact)."""
+    return kv_compact(k_ctx, v_ctx, offsets, idx, stream=stream)
+
+
 def evict(q, k_ctx, k_new, v_ctx, keep_ratio, mode=0, scale=None, stream=None):
     """Score, select and compact: returns (k_out, v_out, offsets, idx, scores)."""
     scores, _ = score(q, k_ctx, k_new, scale=scale, stream=stream)
