@@ -156,3 +156,63 @@ def test_compact_tokens():
             for t, j in enumerate(idx):
                 assert np.array_equal(ko[l, h, t], k[l, h, j])
                 assert np.array_equal(vo[l, h, t], v[l, h, j])
+
+
+# ---- planted mistakes: each must be caught by a pin above -----------------
+def _zscore_sample_std(g, w=E.DEFAULT_WINDOW, eps=E.DEFAULT_EPS):
+    g = np.asarray(g, dtype=np.float64)
+    out = np.zeros(g.shape[0])
+    for t in range(g.shape[0]):
+        win = E.window(t, w)
+        if len(win) > 1:
+            x = g[win.start:win.stop]
+            out[t] = (g[t] - x.mean()) / (x.std(ddof=1) + eps)
+    return out
+
+
+def _zscore_variance(g, w=E.DEFAULT_WINDOW, eps=E.DEFAULT_EPS):
+    g = np.asarray(g, dtype=np.float64)
+    out = np.zeros(g.shape[0])
+    for t in range(g.shape[0]):
+        win = E.window(t, w)
+        if len(win):
+            x = g[win.start:win.stop]
+            out[t] = (g[t] - x.mean()) / (x.var() + eps)
+    return out
+
+
+def _scores_swapped(g_a, g_b, w=E.DEFAULT_WINDOW, eps=E.DEFAULT_EPS, detrend=True):
+    return E.__dict__["_orig_token_scores"](g_b, g_a, w, eps, detrend)
+
+
+def _deltas_l1(h):
+    h = np.asarray(h, dtype=np.float64)
+    g = np.zeros(h.shape[0])
+    g[1:] = np.abs(np.diff(h, axis=0)).sum(axis=1)
+    return g
+
+
+_PINS = [test_deltas_pythagorean, test_window_positions, test_rolling_mean_ramp_closed_form,
+         test_zscore_ramp_closed_form, test_zscore_exact_rationals, test_score_bands]
+
+
+@pytest.mark.parametrize("name,attr,mutant", [
+    ("window excludes t", "window",
+     lambda t, w: range(max(1, t - w), t) if t >= 1 else range(0)),
+    ("window includes position 0", "window",
+     lambda t, w: range(max(0, t - w + 1), t + 1) if t >= 1 else range(0)),
+    ("sample deviation", "rolling_zscore", _zscore_sample_std),
+    ("variance instead of deviation", "rolling_zscore", _zscore_variance),
+    ("bands swapped", "token_scores", _scores_swapped),
+    ("L1 norm of the change", "hidden_deltas", _deltas_l1),
+])
+def test_planted_mistakes_are_caught(monkeypatch, name, attr, mutant):
+    monkeypatch.setitem(E.__dict__, "_orig_token_scores", E.token_scores)
+    monkeypatch.setattr(E, attr, mutant)
+    caught = 0
+    for pin in _PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, ZeroDivisionError):
+            caught += 1
+    assert caught >= 1, f"no pin catches: {name}"

@@ -86,3 +86,45 @@ def test_merge_invalid_source_ignored_and_heads_separate():
     gg = S.soft_cosine_gate(V[0, 1, 3], V[0, 1, 0])
     assert g[2] == gg
     assert np.allclose(vo[1], (V[0, 1, 0] + gg * V[0, 1, 3]) / (1 + gg), atol=1e-15)
+
+
+# ---- planted mistakes: each must be caught by a pin above -----------------
+def _cos(a, b):
+    a, b = np.asarray(a, float), np.asarray(b, float)
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    return 0.0 if na == 0 or nb == 0 else float(a @ b / (na * nb))
+
+
+_PINS = [test_gate_closed_forms, test_gate_matches_scipy_cosine,
+         test_merge_drop_and_uniform_mean, test_merge_partial_weight_closed_form]
+
+
+def _merge_unnormalised(k_ctx, v_ctx, offsets, idx, src_offsets, src_idx):
+    ko, vo, g, m = S.__dict__["_orig_merge"](k_ctx, v_ctx, offsets, idx, src_offsets, src_idx)
+    return ko * (1.0 + m[:, None]), vo * (1.0 + m[:, None]), g, m
+
+
+def _merge_count_weighted(k_ctx, v_ctx, offsets, idx, src_offsets, src_idx):
+    ko, vo, g, m = S.__dict__["_orig_merge"](k_ctx, v_ctx, offsets, idx, src_offsets, src_idx)
+    cnt = np.diff(src_offsets).astype(float)
+    f = (1.0 + m) / (1.0 + cnt)
+    return ko * f[:, None], vo * f[:, None], g, m
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")   # mutants may divide by zero
+@pytest.mark.parametrize("name,attr,mutant", [
+    ("no clamp at 0", "soft_cosine_gate", lambda a, b: _cos(a, b)),
+    ("absolute cosine", "soft_cosine_gate", lambda a, b: abs(_cos(a, b))),
+    ("merge not normalised", "merge_compact", _merge_unnormalised),
+    ("normalised by count", "merge_compact", _merge_count_weighted),
+])
+def test_planted_mistakes_are_caught(monkeypatch, name, attr, mutant):
+    monkeypatch.setitem(S.__dict__, "_orig_merge", S.merge_compact)
+    monkeypatch.setattr(S, attr, mutant)
+    caught = 0
+    for pin in _PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, ZeroDivisionError):
+            caught += 1
+    assert caught >= 1, f"no pin catches: {name}"
