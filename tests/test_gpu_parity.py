@@ -582,3 +582,35 @@ def test_llama8b_128k_chunked_full_size():
             workers=WORKERS)
         check_lse(lse[l, h].cpu().numpy(), l_ref, f"lse[{l},{h}]")
         check_scores(sc[l, h].cpu().numpy(), S, f"scores[{l},{h}]")
+
+
+def test_one_million_key_head():
+    # the largest context here: one head of 2^20 cached keys (8x the 128K
+    # workload), G = 2, from the seeded generator; sampled rows against the
+    # oracle's row definition, every score against the rows' lower bounds,
+    # and the selection as a valid top-k of the GPU scores
+    w = synth.LLAMA8B_8K.shrink(n_c=1 << 20, n_prompt=32, L=1, H=1, G=2, structure="none")
+    _say("case: one head of", w.n_c, "keys")
+    gen = synth.generate_workload(w, workers=WORKERS)
+    dev = _upload(gen)
+    out = _run(w, dev)
+    q, kc, kn = oracle.workload_head_inputs({k: gen[k][0, 0] for k in ("q", "k_ctx", "k_new")})
+    lse_g = out["lse"][0, 0].cpu().numpy()
+    sc_g = out["scores"][0, 0].cpu().numpy().astype(np.float64)
+    k_all = np.concatenate([kc, kn])
+    rng = np.random.default_rng(4)
+    rows = [(g, i) for g in range(w.G) for i in (0, w.n_prompt, w.n_in - 1)]
+    rows += [(int(rng.integers(w.G)), int(rng.integers(w.n_in))) for _ in range(6)]
+    for (g, i) in rows:
+        a, l = oracle.attention_rows(q[g, i][None], np.array([i]), k_all[: w.n_c + i + 1],
+                                     w.n_c, float(w.scale))
+        check_lse(np.array([lse_g[g, i]]), l, f"lse[{g},{i}]")
+        assert np.all(sc_g >= a[0, :w.n_c] * (1 - 2e-3) - 1e-6), f"score below row ({g},{i})"
+    assert np.all(sc_g >= 0) and np.all(sc_g <= 1)
+    k = oracle.keep_count(w.n_c, w.keep_ratio)
+    kept = head_kept(out["offsets"].cpu().numpy(), out["idx"].cpu().numpy(), 0)
+    check_valid_topk(out["scores"][0, 0].cpu().numpy(), kept, k)
+    assert np.array_equal(dev_bf16_bits(out["k_out"]), gen["k_ctx"][0, 0][kept])
+    # the model-wide budget over the same 2^20 scores equals mode 0 here
+    o2, i2 = kvq.kv_topk_select(out["scores"], w.keep_ratio, 2)
+    assert torch.equal(i2, out["idx"]) and torch.equal(o2, out["offsets"])
