@@ -548,7 +548,7 @@ def run_epikv(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "L": w.L, "H": w.H, "d": w.d, "D": w.D, "n": w.n,
                    "budget": w.budget, "band_a": list(w.band_a), "band_b": list(w.band_b),
