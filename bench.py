@@ -67,9 +67,9 @@ def algorithmic_work(w, mode=0, chunk=None):
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` recorded under profiles/ by rocprofv3
     FETCH_SIZE / WRITE_SIZE runs (calibrated against a plain copy), or None
-    if no record matches the library sources as they are now."""
-    from query_agnostic_eviction_amd.build import source_digest
-    digest = source_digest()
+    if no record matches the device code as it is now."""
+    from query_agnostic_eviction_amd.build import kernel_digest
+    digest = kernel_digest()
     prof = os.path.join(ROOT, "profiles")
     if not os.path.isdir(prof):
         return None

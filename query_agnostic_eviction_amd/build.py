@@ -57,6 +57,27 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+# host-only sources: argument checks and dispatch of the C ABI, no device code
+HOST_ONLY = ("kvq_api.hip",)
+
+
+def kernel_digest() -> str:
+    """Digest of the device code alone: every kernel source and its launch
+    shapes, the device headers and the flags.  Hardware-counter records of a
+    kernel stay valid while this is unchanged (the C ABI's host checks and
+    the public header's documentation do not touch the kernels)."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".h")) and f not in HOST_ONLY)
+    for f in files:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(CFLAGS[:-2]).encode())
+    h.update(repr(sorted(EXTRA_FLAGS.items())).encode())
+    return h.hexdigest()
+
+
 STAMP = LIB + ".stamp"
 
 

@@ -287,7 +287,9 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
 int kv_epi_deltas(const void* h, int n_layers, int64_t n, int D, float* g, void* stream) {
   if (!h || !g || n_layers < 1 || n < 1) return KV_ERR_INVALID_ARG;
   if (D < 8 || D > 8192 || D % 8 != 0) return KV_ERR_UNSUPPORTED;
-  if (n >= (int64_t)1 << 36) return KV_ERR_INVALID_ARG;
+  // one workgroup per run of 16 rows of a layer: the grid must stay < 2^31
+  if (n >= (int64_t)1 << 36 || (int64_t)n_layers * ((n + 15) / 16) >= (int64_t)1 << 31)
+    return KV_ERR_INVALID_ARG;
   if (!aligned(h, 16) || !aligned(g, 4)) return KV_ERR_ALIGNMENT;
   (void)hipGetLastError();
   return hip_status(kvq::launch_epi_deltas(static_cast<const uint16_t*>(h), n_layers, n, D, g,

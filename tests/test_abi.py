@@ -224,6 +224,7 @@ def test_epikv_validation(lib):
     assert d(P, 2, 100, 4096, NUL, NUL) == INV
     assert d(P, 0, 100, 4096, P, NUL) == INV
     assert d(P, 2, 0, 4096, P, NUL) == INV
+    assert d(P, 64, 2 ** 30, 4096, P, NUL) == INV      # grid would exceed 2^31 workgroups
     for D in (0, 4, 12, 8200, 16384):
         assert d(P, 2, 100, D, P, NUL) == UNS
     assert d(P2, 2, 100, 4096, P, NUL) == ALN
