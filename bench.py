@@ -113,6 +113,29 @@ def calibration_copy(torch):
     return 2.0 * CALIB_BYTES / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def calibration_gemm(torch, n=8192, reps=400, warm=50):
+    """A plain n x n x n bf16 matrix product through the vendor BLAS
+    (torch.matmul, contiguous operands), run after the timed region for about
+    0.3 s: its TFLOP/s is the practically attainable dense bf16 matrix rate of
+    this part under sustained load, the reference point for the scoring passes'
+    fraction of the nominal peak."""
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), device="cuda", generator=gen).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=gen).to(torch.bfloat16).contiguous()
+    c = torch.matmul(a, b)
+    for _ in range(warm):   # sustained rate, not the first burst
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    flops = 2.0 * n * n * n * reps
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def cold_time_ms(torch, fn, reps=5):
     """Median time of fn() on the current stream, each run preceded by a
     1 GiB write to a scratch buffer so that no input is left in the 256 MB
@@ -336,6 +359,7 @@ def main():
     # a plain device copy of known size after the timed region: under
     # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE calibrate the counters
     copy_gbs = calibration_copy(torch)
+    gemm_tflops = calibration_gemm(torch)
 
     # compaction alone with no input left in the last-level cache
     def compact_only():
@@ -399,6 +423,10 @@ def main():
                                        / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gbs": round(sel_gbs, 1),
         "copy_gbs": round(copy_gbs, 1),
+        # attainable dense bf16 rate (vendor GEMM, 8192^3) and the two
+        # scoring passes' combined rate as a fraction of it
+        "gemm_tflops": round(gemm_tflops, 1),
+        "scoring_frac_of_gemm": round(scoring_tf / gemm_tflops, 4),
     }
     print(json.dumps(line), flush=True)
 
