@@ -132,7 +132,8 @@ int kvscore_chunked_colmax(const void* q, const void* k_ctx, const float* lse,
 
 /* Total kept count for kv_topk_select: L*H*k (mode 0, k = keep count of n_c),
  * L*k_L (mode 1, k_L = keep count of H*n_c) or k_M (mode 2, keep count of
- * L*H*n_c).  Pure host function. */
+ * L*H*n_c).  Pure host function.  Limits: L*H < 2^31, H*n_c < 2^31 and, in
+ * mode 2, L*H*n_c < 2^40 (KV_ERR_INVALID_ARG otherwise). */
 int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
                   int64_t* total_out);
 
@@ -176,7 +177,7 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
  * bit for bit.  total = offsets[L*H] (known on the host from kv_topk_total).
  * offsets must be non-decreasing with offsets[0] = 0; a row whose index falls
  * outside [0, n_c) is written as zeros instead of being read.  d in
- * {64, 128, 256}. */
+ * {64, 128, 256}; L*H < 2^31, n_c < 2^31, 0 <= total <= L*H*n_c. */
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream);

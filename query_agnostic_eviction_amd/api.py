@@ -45,6 +45,13 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _size(t: torch.Tensor, n: int, name: str) -> None:
+    """A caller-supplied output must hold at least the n elements the kernel
+    writes (checked before anything is enqueued)."""
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, {n} needed")
+
+
 def _dev(t: torch.Tensor, dtype, name: str) -> None:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -104,6 +111,7 @@ def kvscore_lse(q: torch.Tensor, k_ctx: torch.Tensor, k_new: torch.Tensor,
     if lse is None:
         lse = torch.empty((L, H, G, n_c + n_prompt), dtype=torch.float32, device=q.device)
     _dev(lse, torch.float32, "lse")
+    _size(lse, L * H * G * (n_c + n_prompt), "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check("kvscore_lse", _lib.load().kvscore_lse(
@@ -125,6 +133,7 @@ def kvscore_colmax(q: torch.Tensor, k_ctx: torch.Tensor, lse: torch.Tensor,
     if scores is None:
         scores = torch.empty((L, H, n_c), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
+    _size(scores, L * H * n_c, "scores")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check("kvscore_colmax", _lib.load().kvscore_colmax(
@@ -183,6 +192,7 @@ def kvscore_chunked_colmax(q, k_ctx, lse, G: int, n_prompt: int, chunk: int,
     if scores is None:
         scores = torch.empty((L, H, n_c), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
+    _size(scores, L * H * n_c, "scores")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _check("kvscore_chunked_colmax", _lib.load().kvscore_chunked_colmax(
@@ -209,6 +219,7 @@ def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
         idx = torch.empty(total, dtype=torch.int32, device=scores.device)
     _dev(offsets, torch.int64, "offsets")
     _dev(idx, torch.int32, "idx")
+    _size(offsets, L * H + 1, "offsets")
     ws_bytes = kv_topk_workspace_bytes(L, H, n_c, mode)
     ws = None
     if ws_bytes:
@@ -263,8 +274,8 @@ def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
         v_out = torch.empty((total, d), dtype=torch.bfloat16, device=k_ctx.device)
     _dev(k_out, torch.bfloat16, "k_out")
     _dev(v_out, torch.bfloat16, "v_out")
-    if k_out.shape[0] < total or v_out.shape[0] < total:
-        raise ValueError("k_out / v_out too small")
+    _size(k_out, total * d, "k_out")
+    _size(v_out, total * d, "v_out")
     _check("kv_compact", _lib.load().kv_compact(
         _ptr(k_ctx), _ptr(v_ctx), _ptr(offsets), _ptr(idx), _ptr(k_out), _ptr(v_out),
         L, H, d, n_c, total, _stream(stream)))

@@ -215,6 +215,8 @@ int kv_topk_total(int L, int H, int64_t n_c, double keep_ratio, int mode,
   if (mode < 0 || mode > 2) return KV_ERR_UNSUPPORTED;
   if ((int64_t)H * n_c >= (int64_t)1 << 31 || (int64_t)L * H >= (int64_t)1 << 31)
     return KV_ERR_INVALID_ARG;
+  // mode 2 counts per workgroup in 32 bits: at most 2^40 scores (4 TiB)
+  if (mode == 2 && (int64_t)L * H * n_c >= (int64_t)1 << 40) return KV_ERR_INVALID_ARG;
   if (mode == 0)
     *total_out = (int64_t)L * H * keep_count_of(n_c, keep_ratio);
   else if (mode == 1)
@@ -271,7 +273,7 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
   if (!k_ctx || !v_ctx || !offsets || !idx || !k_out || !v_out)
     return KV_ERR_INVALID_ARG;
   if (L < 1 || H < 1 || n_c < 1 || total < 0) return KV_ERR_INVALID_ARG;
-  if ((int64_t)L * H >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
+  if ((int64_t)L * H >= (int64_t)1 << 31 || n_c >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
   if (total > (int64_t)L * H * n_c) return KV_ERR_INVALID_ARG;
   if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
   if (!aligned(k_ctx, 16) || !aligned(v_ctx, 16) || !aligned(k_out, 16) ||

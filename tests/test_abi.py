@@ -82,6 +82,10 @@ def test_topk_total(lib):
     assert out.value == oracle.keep_count(48 * 8 * 16384, 0.1)
     assert lib.kv_topk_total(48, 8, 16384, 0.1, 3, ctypes.byref(out)) == UNS
     assert lib.kv_topk_total(0, 8, 16384, 0.1, 0, ctypes.byref(out)) == INV
+    # mode 2 is limited to 2^40 scores in all; modes 0 and 1 are not
+    assert lib.kv_topk_total(2 ** 20, 1, 2 ** 20, 0.1, 2, ctypes.byref(out)) == INV
+    assert lib.kv_topk_total(2 ** 20, 1, 2 ** 20 - 1, 0.1, 2, ctypes.byref(out)) == OK
+    assert lib.kv_topk_total(2 ** 20, 1, 2 ** 20, 0.1, 0, ctypes.byref(out)) == OK
     assert lib.kv_topk_workspace_bytes(32, 8, 8192, 0) == 0
     assert lib.kv_topk_workspace_bytes(32, 8, 8192, 1) == 0
     ws = lib.kv_topk_workspace_bytes(32, 8, 8192, 2)
@@ -173,6 +177,7 @@ def test_compact_validation(lib):
     assert _cmp(lib, d=100) == UNS
     assert _cmp(lib, total=-1) == INV
     assert _cmp(lib, total=401) == INV                # more rows than L*H*n_c
+    assert _cmp(lib, n_c=2 ** 31) == INV              # positions are int32
     assert _cmp(lib, L=0) == INV
     assert _cmp(lib, ko=P4) == ALN
     assert _cmp(lib, off=P4) == ALN
