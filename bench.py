@@ -68,8 +68,10 @@ def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` recorded under profiles/ by rocprofv3
     FETCH_SIZE / WRITE_SIZE runs (calibrated against a plain copy), or None
     if no record matches the device code as it is now."""
-    from query_agnostic_eviction_amd.build import kernel_digest
-    digest = kernel_digest()
+    from query_agnostic_eviction_amd.build import KERNEL_SOURCES, kernel_digest
+    if kernel not in KERNEL_SOURCES:
+        return None
+    digest = kernel_digest(kernel)
     prof = os.path.join(ROOT, "profiles")
     if not os.path.isdir(prof):
         return None

@@ -59,22 +59,39 @@ def source_digest() -> str:
 
 # host-only sources: argument checks and dispatch of the C ABI, no device code
 HOST_ONLY = ("kvq_api.hip",)
+# headers every kernel source includes
+DEVICE_HEADERS = ("kvq_device.h", "kvq_internal.h")
+# the source file that holds the kernels of each entry point
+KERNEL_SOURCES = {
+    "kvscore_lse": "kvscore_lse.hip", "kvscore_colmax": "kvscore_colmax.hip",
+    "kv_topk_select": "kv_topk.hip", "kv_head_scores": "kv_topk.hip",
+    "kv_select_tokens": "kv_topk.hip", "kv_compact": "kv_compact.hip",
+    "kv_compact_tokens": "kv_compact.hip", "kv_epi_deltas": "epikv.hip",
+    "kv_epi_scores": "epikv.hip", "kv_merge_compact": "selkv_merge.hip",
+}
 
 
-def kernel_digest() -> str:
-    """Digest of the device code alone: every kernel source and its launch
-    shapes, the device headers and the flags.  Hardware-counter records of a
-    kernel stay valid while this is unchanged (the C ABI's host checks and
-    the public header's documentation do not touch the kernels)."""
+def kernel_digest(entry: str = None) -> str:
+    """Digest of device code: with `entry`, the source holding that entry
+    point's kernels plus the device headers and the flags it is built with;
+    without, every kernel source.  A hardware-counter record of a kernel
+    stays valid while its digest is unchanged (the C ABI's host checks, the
+    public header's documentation and the other kernels do not touch it)."""
+    if entry is None:
+        files = sorted(f for f in os.listdir(CSRC)
+                       if f.endswith((".hip", ".h")) and f not in HOST_ONLY)
+        extra = sorted(EXTRA_FLAGS.items())
+    else:
+        src = KERNEL_SOURCES[entry]
+        files = [src, *DEVICE_HEADERS]
+        extra = EXTRA_FLAGS.get(src, [])
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC)
-                   if f.endswith((".hip", ".h")) and f not in HOST_ONLY)
     for f in files:
         h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     h.update(" ".join(CFLAGS[:-2]).encode())
-    h.update(repr(sorted(EXTRA_FLAGS.items())).encode())
+    h.update(repr(extra).encode())
     return h.hexdigest()
 
 
