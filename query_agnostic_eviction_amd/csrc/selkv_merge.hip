@@ -50,7 +50,8 @@ constexpr int kMergeLdsHeads = 512;   // offsets staged in LDS up to this many h
 
 // A row group of D/8 lanes owns one kept row (8 elements, one 16-byte load
 // per lane and row); a wave holds 512/D rows.  Routed rows are read kBatch at
-// a time so that their loads overlap.
+// a time so that their loads overlap; lanes whose list is exhausted are
+// masked off the loads (the wave iterates over its longest list).
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(
     const uint16_t* __restrict__ k_ctx, const uint16_t* __restrict__ v_ctx,
@@ -121,9 +122,16 @@ __global__ __launch_bounds__(256) void merge_kernel(
       in[u] = sb < s1;
       const int64_t j = in[u] ? src_idx[sb] : -1;
       ok[u] = row_ok && in[u] && j >= 0 && j < n_c;
-      const int64_t jj = ok[u] ? j : jt_safe;  // a valid row; data unused if !ok
-      kr[u] = ldg16(kh + jj * D);
-      vr[u] = ldg16(vh + jj * D);
+      // a lane past the end of its list (or with a rejected position)
+      // issues no load: rows of a wave hold lists of different lengths, and
+      // the wave runs to the longest of them
+      if (ok[u]) {
+        kr[u] = ldg16(kh + j * D);
+        vr[u] = ldg16(vh + j * D);
+      } else {
+        kr[u] = u32x4{0, 0, 0, 0};
+        vr[u] = u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
