@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void epi_deltas_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + 256 * i;
-      dst[i] = c < cpr ? ldg16(row + c * 8) : u32x4{0, 0, 0, 0};
+      dst[i] = c < cpr ? ldg16_once(row + c * 8) : u32x4{0, 0, 0, 0};
     }
   };
 

@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void compact_kernel(
     const int64_t r = src_row[it * RPI + rr];
     const size_t src = (size_t)(r < 0 ? 0 : r) * D + c * 8;
     const uint32_t keep = r < 0 ? 0u : 0xffffffffu;
-    kv[it] = ldg16(k_ctx + src) & keep;
-    vv[it] = ldg16(v_ctx + src) & keep;
+    kv[it] = ldg16_once(k_ctx + src) & keep;
+    vv[it] = ldg16_once(v_ctx + src) & keep;
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {

@@ -39,6 +39,12 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// 16-byte load of data read exactly once (streams and gathers): marked
+// non-temporal so that it does not displace reused lines in the caches
+__device__ __forceinline__ u32x4 ldg16_once(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;

@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
   if (!active) s1 = s0;
 
   float ks[8], vs[8], vt[8];
-  widen8(ldg16(kh + jt_safe * D), ks);
-  widen8(ldg16(vh + jt_safe * D), vt);
+  widen8(ldg16_once(kh + jt_safe * D), ks);
+  widen8(ldg16_once(vh + jt_safe * D), vt);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (!row_ok) ks[e] = vt[e] = 0.f;
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
       // issues no load: rows of a wave hold lists of different lengths, and
       // the wave runs to the longest of them
       if (ok[u]) {
-        kr[u] = ldg16(kh + j * D);
-        vr[u] = ldg16(vh + j * D);
+        kr[u] = ldg16_once(kh + j * D);
+        vr[u] = ldg16_once(vh + j * D);
       } else {
         kr[u] = u32x4{0, 0, 0, 0};
         vr[u] = u32x4{0, 0, 0, 0};
