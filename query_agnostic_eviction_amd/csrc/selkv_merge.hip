@@ -51,7 +51,9 @@ constexpr int kMergeLdsHeads = 512;   // offsets staged in LDS up to this many h
 // A row group of D/8 lanes owns one kept row (8 elements, one 16-byte load
 // per lane and row); a wave holds 512/D rows.  Routed rows are read kBatch at
 // a time so that their loads overlap; lanes whose list is exhausted are
-// masked off the loads (the wave iterates over its longest list).
+// masked off the loads (the wave iterates over its longest list), and the
+// workgroup hands its rows to the waves longest list first, so that rows of
+// similar length share a wave.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(
     const uint16_t* __restrict__ k_ctx, const uint16_t* __restrict__ v_ctx,
@@ -62,8 +64,37 @@ __global__ __launch_bounds__(256) void merge_kernel(
   constexpr int LPR = D / 8;     // lanes per row
   constexpr int RPW = 64 / LPR;  // rows per wave
   __shared__ int64_t off_lds[kMergeLdsHeads];
+  constexpr int RPB = 4 * RPW;   // rows per workgroup
+  __shared__ int cnt_lds[RPB], perm[RPB];
   const int lane = threadIdx.x & 63, sub = lane % LPR;
-  const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  // rows of the workgroup ordered by the length of their routed list
+  // (longest first, ties by position), so that the rows sharing a wave have
+  // similar lengths: a wave runs to the longest list among its rows
+  const int64_t t_base = (int64_t)blockIdx.x * RPB;
+  if (threadIdx.x < RPB) {
+    const int64_t r = t_base + threadIdx.x;
+    int c = -1;  // rows past the end sort last
+    if (r < total) {
+      int64_t a0 = src_offsets[r], a1 = src_offsets[r + 1];
+      a0 = a0 < 0 ? 0 : (a0 > n_src ? n_src : a0);
+      a1 = a1 < a0 ? a0 : (a1 > n_src ? n_src : a1);
+      const int64_t len = a1 - a0;
+      c = len > (1 << 30) ? (1 << 30) : (int)len;
+    }
+    cnt_lds[threadIdx.x] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x < RPB) {
+    const int ci = cnt_lds[threadIdx.x];
+    int rank = 0;
+    for (int j = 0; j < RPB; ++j) {
+      const int cj = cnt_lds[j];
+      rank += (cj > ci || (cj == ci && j < (int)threadIdx.x)) ? 1 : 0;
+    }
+    perm[rank] = threadIdx.x;
+  }
+  __syncthreads();
+  const int64_t t = t_base + perm[(threadIdx.x >> 6) * RPW + lane / LPR];
   const bool active = t < total;
   const int64_t tt = active ? t : total - 1;  // inactive groups shadow a valid row
   // head of row tt: the largest lh with offsets[lh] <= tt, searched in LDS
