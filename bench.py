@@ -75,7 +75,8 @@ def recorded_traffic(kernel: str, workload: str):
     prof = os.path.join(ROOT, "profiles")
     if not os.path.isdir(prof):
         return None
-    for name in sorted(os.listdir(prof)):
+    own = f"kvq_kernels_{workload}_traffic.md"   # this workload's own profile first
+    for name in sorted(os.listdir(prof), key=lambda n: (n != own, n)):
         if not name.endswith("_traffic.md"):
             continue
         with open(os.path.join(prof, name)) as fh:
