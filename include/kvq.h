@@ -156,7 +156,8 @@ size_t kv_topk_workspace_bytes(int L, int H, int64_t n_c, int mode);
  * needs the workspace of kv_topk_workspace_bytes.  Writes
  * offsets[L*H + 1] (offsets[l*H + h] = first kept row of that head) and the
  * kept positions j into idx, ascending within each head.  scores must be
- * non-negative (they are ordered by their IEEE bit pattern).  capacity is the
+ * non-negative (they are ordered by their IEEE bit pattern, with -0.0 read
+ * as +0.0).  capacity is the
  * length of idx; KV_ERR_CAPACITY if it is below the total (kv_topk_total). */
 int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
                    double keep_ratio, int mode, int64_t* offsets, int32_t* idx,

@@ -54,11 +54,12 @@ __device__ __forceinline__ int block_excl_scan(int x, int* sm, int* total) {
 
 // Order-preserving map of a float's bits to uint32: identity for the
 // non-negative scores of the attention path; for signed scores the usual
-// sign flip, with -0.0 folded onto +0.0 so that equal values tie.
+// sign flip.  In both, -0.0 is folded onto +0.0 so that equal values tie
+// (without it a -0.0 score would rank above every positive one).
 template <bool SIGNED>
 __device__ __forceinline__ uint32_t sort_key(uint32_t v) {
+  if (v == 0x80000000u) v = 0u;  // -0.0 ties with +0.0 in both orders
   if (!SIGNED) return v;
-  if (v == 0x80000000u) v = 0u;
   return (v & 0x80000000u) ? ~v : (v | 0x80000000u);
 }
 

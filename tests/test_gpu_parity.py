@@ -168,6 +168,32 @@ def test_select_ties_bit_exact(n_c, L, H):
             assert np.array_equal(i.cpu().numpy(), ri), (mode, r)
 
 
+@pytest.mark.parametrize("n_c,L,H", [(5000, 2, 3), (8193, 1, 2), (9, 2, 2)])
+def test_select_signed_zero_ties_with_zero(n_c, L, H):
+    """A -0.0 score equals +0.0: it ties with the zeros by position instead of
+    ranking above every positive score (its sign bit would otherwise put it
+    first in the bit-pattern order)."""
+    rng = np.random.default_rng(31 + n_c)
+    s = (rng.integers(0, 4, size=(L, H, n_c)).astype(np.float32) / 4.0)
+    zeros = s == 0.0
+    flip = zeros & (rng.random(s.shape) < 0.5)
+    s[flip] = -0.0
+    assert np.signbit(s).any() and (s == 0).sum() > np.signbit(s).sum()
+    dev = torch.from_numpy(s).cuda()
+    for mode in (0, 1, 2):
+        for r in (0.1, 0.6, 0.9, 1.0):
+            o, i = kvq.kv_topk_select(dev, r, mode)
+            ro, ri = oracle.select(s, r, mode)
+            assert np.array_equal(o.cpu().numpy(), ro), (mode, r)
+            assert np.array_equal(i.cpu().numpy(), ri), (mode, r)
+    # the signed token select folds -0.0 the same way
+    flat = torch.from_numpy(s.reshape(-1)).cuda()
+    k = max(1, s.size * 3 // 4)
+    got = kvq.kv_select_tokens(flat, k).cpu().numpy()
+    want = oracle.epikv.select_tokens(s.reshape(-1).astype(np.float64), k)
+    assert np.array_equal(got, want)
+
+
 def test_select_distinct_bit_patterns():
     # scores spanning many exponents, including exact zeros and 1.0
     rng = np.random.default_rng(5)

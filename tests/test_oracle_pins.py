@@ -467,3 +467,16 @@ def test_chunked_brute_force(seed):
         np.testing.assert_allclose(lse[qo:qo + G * n_in], np.ravel(lb), rtol=1e-12, atol=1e-12)
         qo += G * n_in
         ko += n_in
+
+
+def test_select_signed_zero_equals_zero():
+    """-0.0 and +0.0 are the same score: with zeros at the cut, the kept
+    zeros are the lowest positions, whatever their sign bits (KVzip section
+    4.1 ranks by score value; ties go to the lower index)."""
+    s = np.array([[[0.5, -0.0, 0.0, -0.0, 0.25, 0.0]]], dtype=np.float32)
+    # keep 4 of 6: 0.5, 0.25, then the two lowest-position zeros (1 and 2)
+    off, idx = oracle.select(s, 4 / 6 + 1e-9, 0)
+    assert off.tolist() == [0, 4] and idx.tolist() == [0, 1, 2, 4]
+    assert oracle.epikv.select_tokens(s.reshape(-1), 4).tolist() == [0, 1, 2, 4]
+    s2 = np.abs(s)
+    assert np.array_equal(oracle.select(s2, 4 / 6 + 1e-9, 0)[1], idx)
