@@ -48,8 +48,10 @@
  *     stream).  A launch failure returns KV_ERR_HIP and records the HIP error
  *     for kv_last_hip_error(); faults during execution surface at the
  *     caller's next synchronisation.
- *   - Inputs must be finite.  Calls are reentrant; calls that write the same
- *     buffers must not overlap.
+ *   - Inputs must be finite, and so must the logits scale * <q, k> that the
+ *     scoring passes form in fp32 (any bf16 inputs of model scale qualify).
+ *     Calls are reentrant; calls that write the same buffers must not
+ *     overlap.
  */
 #ifndef KVQ_H
 #define KVQ_H
