@@ -235,8 +235,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path is built and timed on a "
-              "single MI355X (every (layer, KV head) is independent; see the "
-              "sharding notes in the design document). Run with --gpus 1.",
+              "single MI355X. Every (layer, KV head) is independent, so several "
+              "GPUs would each score their own share of the heads. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -24,8 +24,7 @@ Cache Compression with Context Reconstruction"):
   n_in x (m + n_in) attention over the chunk's cached keys and new keys.
 * Section 4.1 (eviction structure): keep the r% highest-scoring KV pairs.
 
-Readings taken where the page is silent (each one is listed with its reason in
-the project's design notes):
+Readings taken where the page is silent:
   - the softmax logits carry the model's 1/sqrt(d) temperature; it is passed
     in as `scale` (the same float32 value the GPU receives);
   - the pass is causal over the new tokens: query row i (0-based) sees every
