@@ -244,7 +244,7 @@ def test_epikv_r1_8b_64k_full_size():
         assert torch.equal(vo[l, h].view(torch.int16), vc[l, h][idx_dev.long()].view(torch.int16))
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(40))
 def test_random_shapes(i):
     rng = np.random.default_rng(7000 + i)
     n = int(rng.choice([1, 2, 63, 64, 65, int(rng.integers(2, 5000))]))

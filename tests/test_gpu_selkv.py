@@ -176,7 +176,7 @@ def test_many_heads_global_search():
     check_merge(kb, vb, off, idx, so, si, got)
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(30))
 def test_random_shapes(i):
     rng = np.random.default_rng(8000 + i)
     L, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))

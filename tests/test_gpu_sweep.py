@@ -15,7 +15,7 @@ from parity_util import (check_lse, check_scores, check_topk_band, dev_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 160
 
 
 def _say(*a):
