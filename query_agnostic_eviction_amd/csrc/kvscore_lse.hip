@@ -6,11 +6,11 @@
 // lse[l][h][g][i] = ln sum_{seen j} exp(scale * <q_{g,i}, k_j>).
 //
 // Mapping on gfx950:
-//  * A workgroup of 4 waves owns 8 query fragments of 32 rows each (4 at
-//    d = 256; a fragment is 32 consecutive positions of one query head g;
-//    fragments of a head are numbered b * G + g over 32-position blocks b).
-//    Each wave keeps its two fragments' queries (one at d = 256, so that two
-//    waves fit per SIMD) in registers for the whole key sweep.
+//  * A workgroup of 4 waves owns 8 query fragments of 32 rows each (a
+//    fragment is 32 consecutive positions of one query head g; fragments of
+//    a head are numbered b * G + g over 32-position blocks b).  Each wave
+//    keeps its two fragments' queries in registers for the whole key sweep,
+//    so every key operand read from LDS feeds two matrix ops.
 //  * Keys stream through LDS in 32 KB tiles (16384 / d keys), double-buffered
 //    and filled by LDS-DMA straight from HBM while the previous tile is in
 //    use: first the cached keys, then the new keys up to the workgroup's last
@@ -25,7 +25,11 @@
 //  * Subtile sums enter each lane's running sum with Kahan compensation
 //    (per subtile, not per logit), so 128K-key rows stay at fp32 accuracy.
 //  * The loop is software-pipelined by one 32-key subtile so the matrix
-//    cores and the VALU/transcendental units work at the same time.
+//    cores and the VALU/transcendental units work at the same time.  At
+//    d = 256 the second set of accumulators would not fit beside two
+//    fragments' queries at two waves per SIMD, so there each subtile is
+//    reduced right after its own matrix ops (the other wave on the SIMD
+//    provides the overlap).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -39,9 +43,11 @@ struct LseCfg {
   static constexpr int KT = Tile<D>::ROWS;  // keys per tile
   static constexpr int NSUB = KT / 32;      // 32-key subtiles per tile
   static constexpr int KS = D / 16;         // k-steps of the 32x32x16 op
-  // query fragments per wave: two share each key operand read, but at
-  // d = 256 their registers would leave one wave per SIMD, so one
-  static constexpr int NFQ = D == 256 ? 1 : 2;
+  // query fragments per wave: two share each key operand read
+  static constexpr int NFQ = 2;
+  // one-subtile software pipeline (a second set of accumulators); off at
+  // d = 256, where it would not fit at two waves per SIMD
+  static constexpr bool PIPE = D != 256;
   static constexpr int FPW = 4 * NFQ;      // fragments per workgroup
 };
 
@@ -235,9 +241,13 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
 #pragma unroll
       for (int f = 0; f < NFQ; ++f) c[f] = mfma32(a, bq[f][s], c[f]);
     }
-    accumulate(p);
+    if constexpr (C::PIPE) {
+      accumulate(p);
 #pragma unroll
-    for (int f = 0; f < NFQ; ++f) p[f] = c[f];
+      for (int f = 0; f < NFQ; ++f) p[f] = c[f];
+    } else {
+      accumulate(c);
+    }
   };
 
   // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
   }
-  accumulate(p);
+  if constexpr (C::PIPE) accumulate(p);
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll
