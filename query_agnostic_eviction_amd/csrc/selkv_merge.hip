@@ -45,12 +45,13 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-constexpr int kBatch = 2;  // routed rows loaded together
+constexpr int kBatch = 1;  // routed rows per step (more costs registers and waves)
 constexpr int kMergeLdsHeads = 512;   // offsets staged in LDS up to this many heads
 
 // A row group of D/8 lanes owns one kept row (8 elements, one 16-byte load
 // per lane and row); a wave holds 512/D rows.  Routed rows are read kBatch at
-// a time so that their loads overlap; lanes whose list is exhausted are
+// a time (one: with ~68 VGPRs, many waves per SIMD keep enough loads in
+// flight, and larger batches measured slower); lanes whose list is exhausted are
 // masked off the loads (the wave iterates over its longest list), and the
 // workgroup hands its rows to the waves longest list first, so that rows of
 // similar length share a wave.
