@@ -5,7 +5,7 @@
 //   k_out[t] = k_ctx[l][h][idx[t]],  v_out[t] = v_ctx[l][h][idx[t]]
 //   for t in [offsets[l*H+h], offsets[l*H+h+1])
 //
-// A pure HBM-bound gather: each workgroup copies 64 consecutive output rows
+// A pure HBM-bound gather: each workgroup copies 32 consecutive output rows
 // of K and V with 16-byte vector loads and stores (a row of d bf16 values is
 // d/8 such chunks, contiguous in memory).  One wave first resolves each
 // row's source (head by binary search of the CSR offsets, then its index)
@@ -18,7 +18,9 @@
 namespace kvq {
 namespace {
 
-constexpr int kCpRows = 64;  // output rows per workgroup
+constexpr int kCpRows = 32;  // output rows per workgroup (the fewest that
+                             // still fill one pass of the block at d = 64;
+                             // 2-3 % faster cold than 64, 128 is slower)
 
 // SHARED: one kept set idx[0..shared_k) for every head (token-level
 // eviction); output row t is head t / shared_k, entry t % shared_k, and the
@@ -32,6 +34,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 256 / CPR;      // rows per pass of the block
   constexpr int IT = kCpRows / RPI;
+  static_assert(IT >= 1 && IT * RPI == kCpRows, "whole passes of the block per workgroup");
 
   __shared__ int64_t src_row[kCpRows];  // lh * n_c + idx, or -1 for a zero row
 
