@@ -180,7 +180,8 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
  * bit for bit.  total = offsets[L*H] (known on the host from kv_topk_total).
  * offsets must be non-decreasing with offsets[0] = 0; a row whose index falls
  * outside [0, n_c) is written as zeros instead of being read.  d in
- * {64, 128, 256}; L*H < 2^31, n_c < 2^31, 0 <= total <= L*H*n_c. */
+ * {64, 128, 256}; L*H < 2^31, n_c < 2^31, 0 <= total <= L*H*n_c.  With
+ * total = 0 nothing is enqueued and idx, k_out and v_out may be NULL. */
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream);
@@ -200,7 +201,8 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
  * every list empty the call equals kv_compact.  src_offsets int64 [total+1]
  * non-decreasing from 0 to n_src (ranges are clamped to [0, n_src)); kept
  * rows with an index outside [0, n_c) come out as zeros.  d in
- * {64, 128, 256}. */
+ * {64, 128, 256}.  With total = 0 nothing is enqueued and idx, k_out and
+ * v_out may be NULL (src_offsets still holds its one entry). */
 int kv_merge_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                      const int32_t* idx, const int64_t* src_offsets,
                      const int32_t* src_idx, void* k_out, void* v_out, float* gate,
@@ -264,7 +266,8 @@ int kv_select_tokens(const float* scores, int64_t n, int64_t k, int32_t* idx,
 
 /* Token-level compaction: k_out[l][h][t] = k_cache[l][h][idx[t]] and the
  * same for v, bit for bit, for t < k, every (l, h).  An index outside
- * [0, n) gives a zero row.  0 <= k <= n; d in {64, 128, 256}. */
+ * [0, n) gives a zero row.  0 <= k <= n; d in {64, 128, 256}.  With k = 0
+ * nothing is enqueued and idx, k_out and v_out may be NULL. */
 int kv_compact_tokens(const void* k_cache, const void* v_cache,
                       const int32_t* idx, void* k_out, void* v_out, int L,
                       int H, int d, int64_t n, int64_t k, void* stream);

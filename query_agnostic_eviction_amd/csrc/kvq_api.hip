@@ -270,8 +270,9 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream) {
-  if (!k_ctx || !v_ctx || !offsets || !idx || !k_out || !v_out)
-    return KV_ERR_INVALID_ARG;
+  if (!k_ctx || !v_ctx || !offsets) return KV_ERR_INVALID_ARG;
+  // an empty kept set has empty (possibly null) idx and outputs
+  if (total > 0 && (!idx || !k_out || !v_out)) return KV_ERR_INVALID_ARG;
   if (L < 1 || H < 1 || n_c < 1 || total < 0) return KV_ERR_INVALID_ARG;
   if ((int64_t)L * H >= (int64_t)1 << 31 || n_c >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
   if (total > (int64_t)L * H * n_c) return KV_ERR_INVALID_ARG;
@@ -279,6 +280,7 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
   if (!aligned(k_ctx, 16) || !aligned(v_ctx, 16) || !aligned(k_out, 16) ||
       !aligned(v_out, 16) || !aligned(offsets, 8) || !aligned(idx, 4))
     return KV_ERR_ALIGNMENT;
+  if (total == 0) return KV_OK;
   (void)hipGetLastError();
   return hip_status(kvq::launch_compact(
       static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx),
@@ -331,7 +333,8 @@ int kv_select_tokens(const float* scores, int64_t n, int64_t k, int32_t* idx,
 int kv_compact_tokens(const void* k_cache, const void* v_cache, const int32_t* idx,
                       void* k_out, void* v_out, int L, int H, int d, int64_t n, int64_t k,
                       void* stream) {
-  if (!k_cache || !v_cache || !idx || !k_out || !v_out) return KV_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache) return KV_ERR_INVALID_ARG;
+  if (k > 0 && (!idx || !k_out || !v_out)) return KV_ERR_INVALID_ARG;
   if (L < 1 || H < 1 || n < 1 || k < 0 || k > n) return KV_ERR_INVALID_ARG;
   if ((int64_t)L * H >= (int64_t)1 << 31 || n >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;
   if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
@@ -350,8 +353,8 @@ int kv_merge_compact(const void* k_ctx, const void* v_ctx, const int64_t* offset
                      const int32_t* idx, const int64_t* src_offsets, const int32_t* src_idx,
                      void* k_out, void* v_out, float* gate, float* mass, int L, int H, int d,
                      int64_t n_c, int64_t total, int64_t n_src, void* stream) {
-  if (!k_ctx || !v_ctx || !offsets || !idx || !src_offsets || !k_out || !v_out)
-    return KV_ERR_INVALID_ARG;
+  if (!k_ctx || !v_ctx || !offsets || !src_offsets) return KV_ERR_INVALID_ARG;
+  if (total > 0 && (!idx || !k_out || !v_out)) return KV_ERR_INVALID_ARG;
   if (n_src > 0 && !src_idx) return KV_ERR_INVALID_ARG;
   if (L < 1 || H < 1 || n_c < 1 || total < 0 || n_src < 0) return KV_ERR_INVALID_ARG;
   if ((int64_t)L * H >= (int64_t)1 << 31 || n_c >= (int64_t)1 << 31) return KV_ERR_INVALID_ARG;

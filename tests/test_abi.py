@@ -182,6 +182,12 @@ def test_compact_validation(lib):
     assert _cmp(lib, ko=P4) == ALN
     assert _cmp(lib, off=P4) == ALN
     assert _cmp(lib, idx=P2) == ALN
+    # an empty kept set: nothing is enqueued and its empty buffers may be null
+    assert _cmp(lib, total=0) == OK
+    assert _cmp(lib, idx=NUL, ko=NUL, vo=NUL, total=0) == OK
+    for name in ("kc", "vc", "off"):
+        assert _cmp(lib, **{name: NUL}, total=0) == INV
+    assert _cmp(lib, total=0, d=96) == UNS
 
 
 def test_binding_rejects_host_tensors():
@@ -268,6 +274,9 @@ def test_epikv_validation(lib):
     assert c(P, P, P, P4, P, 2, 2, 128, 100, 10, NUL) == ALN
     assert c(P, P, P2, P, P, 2, 2, 128, 100, 10, NUL) == ALN
     assert c(P, P, P, P, P, 2, 2, 128, 100, 0, NUL) == OK      # nothing to copy, no launch
+    assert c(P, P, NUL, NUL, NUL, 2, 2, 128, 100, 0, NUL) == OK   # empty buffers may be null
+    assert c(P, P, NUL, P, P, 2, 2, 128, 100, 10, NUL) == INV
+    assert c(P, NUL, NUL, NUL, NUL, 2, 2, 128, 100, 0, NUL) == INV
 
 
 def test_merge_validation(lib):
@@ -281,6 +290,8 @@ def test_merge_validation(lib):
     assert call(si=NUL) == INV
     assert call(si=NUL, n_src=0, total=0) == OK          # nothing to do, no launch
     assert call(g=NUL, m=NUL, total=0) == OK
+    assert call(idx=NUL, ko=NUL, vo=NUL, si=NUL, g=NUL, m=NUL, total=0, n_src=0) == OK
+    assert call(so=NUL, total=0, n_src=0) == INV
     assert call(total=401) == INV
     assert call(n_src=-1) == INV
     assert call(d=96) == UNS

@@ -47,3 +47,28 @@ def test_undersized_outputs_are_rejected():
     ko, vo = kvq.kv_compact(kc, vc, offsets, idx)
     torch.cuda.synchronize()
     assert ko.shape == (total, d) and vo.shape == (total, d)
+
+
+def test_empty_kept_sets():
+    """An empty kept set is a valid request: the calls return empty outputs
+    (empty tensors may carry a null data pointer) and enqueue nothing."""
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    print("empty kept sets", flush=True)
+    dev = "cuda"
+    L, H, n_c, d = 2, 3, 50, 128
+    kc = torch.randn((L, H, n_c, d), device=dev).to(torch.bfloat16)
+    vc = torch.randn((L, H, n_c, d), device=dev).to(torch.bfloat16)
+    offsets = torch.zeros(L * H + 1, dtype=torch.int64, device=dev)
+    idx = torch.empty(0, dtype=torch.int32, device=dev)
+    ko, vo = kvq.kv_compact(kc, vc, offsets, idx)
+    assert ko.shape == (0, d) and vo.shape == (0, d)
+    src_offsets = torch.zeros(1, dtype=torch.int64, device=dev)
+    ko, vo, gate, mass = kvq.kv_merge_compact(kc, vc, offsets, idx, src_offsets, idx)
+    assert ko.shape == (0, d) and gate.numel() == 0 and mass.numel() == 0
+    ko, vo = kvq.kv_compact_tokens(kc, vc, idx)
+    assert ko.shape == (L, H, 0, d) and vo.shape == (L, H, 0, d)
+    # the library's state is untouched: a real compaction right after still matches
+    keep = torch.tensor([0, 7, 49], dtype=torch.int32, device=dev)
+    ko, vo = kvq.kv_compact_tokens(kc, vc, keep)
+    torch.cuda.synchronize()
+    assert torch.equal(ko, kc[:, :, keep.long()]) and torch.equal(vo, vc[:, :, keep.long()])
