@@ -12,3 +12,4 @@ from .generate import (bf16_bits_to_f32, chunk_rows, default_workers,
 from .epikv import (EPI_ALL, EPI_BY_NAME, EPIKV_R1_8B_64K, EPIKV_TINY, EpiWorkload,
                     generate_hidden, generate_hidden_layer, generate_kv)
 from .routing import nearest_position_routes
+from .extreme import PROFILES as EXTREME_PROFILES, generate_extreme_workload

@@ -127,6 +127,34 @@ def test_ragged_shapes(case):
         _select_checks(w, gen, out, S_ref, [(l, h) for l in range(L) for h in range(H)], mode)
 
 
+EXTREME = [
+    # (G, d, n_c, n_prompt, H)
+    (2, 64, 300, 5, 2),
+    (4, 128, 1000, 32, 1),
+    (2, 256, 500, 8, 1),
+]
+
+
+@pytest.mark.parametrize("profile", synth.EXTREME_PROFILES)
+@pytest.mark.parametrize("case", EXTREME, ids=[f"G{c[0]}-d{c[1]}-nc{c[2]}" for c in EXTREME])
+def test_extreme_logit_ranges(case, profile):
+    """Cached-key norms rising or falling 150-fold along the context, or a few
+    keys 40-120x above the rest: logits span hundreds of natural-log units, so
+    pass 1 raises its running max many times mid-sweep (rising, spikes) or
+    sums mostly underflowing terms (falling), and pass 2 subtracts lse values
+    near 750 from logits of the same size."""
+    G, d, n_c, n_p, H = case
+    _say("case: extreme", profile, case)
+    w = synth.LLAMA8B_8K.shrink(G=G, d=d, n_c=n_c, n_prompt=n_p, L=1, H=H, rank=8)
+    gen = synth.generate_extreme_workload(profile, 1, H, G, d, n_c, n_p)
+    out = _run(w, _upload(gen))
+    assert np.all(np.isfinite(out["lse"].cpu().numpy()))
+    sc = out["scores"].cpu().numpy()
+    assert np.all((sc >= 0) & (sc <= 1))
+    S_ref = _full_check(w, gen, out)
+    _select_checks(w, gen, out, S_ref, [(0, h) for h in range(H)], 0)
+
+
 def test_zero_queries_closed_form():
     w = synth.LLAMA8B_8K.shrink(n_c=1500, n_prompt=9, L=1, H=2)
     gen = synth.generate_workload(w, workers=1)

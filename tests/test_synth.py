@@ -120,3 +120,21 @@ def test_nearest_position_routes():
         for t in rows:
             for j in si[so[t]:so[t + 1]]:
                 assert abs(j - idx[t]) == np.abs(k - j).min()
+
+
+def test_extreme_profiles_seeded_and_shaped():
+    """The extreme-logit inputs are reproducible per (l, h) and their cached-key
+    norms follow the requested profile."""
+    for prof in synth.EXTREME_PROFILES:
+        a = synth.generate_extreme_workload(prof, 1, 2, 2, 64, 300, 5)
+        b = synth.generate_extreme_workload(prof, 1, 2, 2, 64, 300, 5)
+        for k in a:
+            assert np.array_equal(a[k], b[k])
+        assert not np.array_equal(a["k_ctx"][0, 0], a["k_ctx"][0, 1])
+        norms = np.linalg.norm(synth.bf16_bits_to_f32(a["k_ctx"][0, 0]).astype(np.float64), axis=1)
+        if prof == "rising":
+            assert norms[-30:].mean() > 10 * norms[:30].mean()
+        elif prof == "falling":
+            assert norms[:30].mean() > 10 * norms[-30:].mean()
+        else:
+            assert np.sum(norms > 20 * np.median(norms)) >= 1
