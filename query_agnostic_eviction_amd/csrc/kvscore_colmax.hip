@@ -12,7 +12,8 @@
 // Mapping on gfx950:
 //  * A workgroup of 4 waves owns 384 cached keys (3 fragments of 32 per
 //    wave, kept in registers as the B operand; 256 keys in 2 fragments at
-//    d = 256, so that two waves fit per SIMD); it sweeps all G * n_in query
+//    d = 256, so that two waves fit per SIMD, and where 384-key workgroups
+//    would leave much padding); it sweeps all G * n_in query
 //    rows of its head in 32 KB tiles (16384 / d rows), double-buffered and
 //    filled by LDS-DMA straight from HBM together with the rows' lse.
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
@@ -29,25 +30,27 @@
 namespace kvq {
 namespace {
 
-template <int D>
+// NF_: cached-key fragments of 32 per wave; each operand read from LDS feeds
+// NF_ matrix ops.  Three by default; two at d = 256, so that two waves fit
+// per SIMD, and also where three would leave much of the last workgroup of
+// each work item padding (see colmax_fragments).
+template <int D, int NF_>
 struct ColCfg {
   static constexpr int QT = Tile<D>::ROWS;  // query rows per tile
   static constexpr int NSUB = QT / 32;
   static constexpr int KS = D / 16;
   static constexpr int LSE_LOADS = QT / 64;  // 4-byte DMA instructions per tile
-  // cached-key fragments of 32 per wave: each operand read from LDS feeds NF
-  // matrix ops; at d = 256 two, so that two waves fit per SIMD
-  static constexpr int NF = D == 256 ? 2 : 3;
+  static constexpr int NF = NF_;
   static constexpr int KEYS_PER_WG = 4 * NF * 32;
 };
 
-template <int D>
+template <int D, int NF_>
 __global__ __launch_bounds__(256, 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const float* __restrict__ lse, float* __restrict__ scores,
     const ScoreShape sh, int wg_per_head, float c2, float inv_scale) {
   const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
-  using C = ColCfg<D>;
+  using C = ColCfg<D, NF_>;
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[2 * TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) float sl[2 * C::QT];
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
   constexpr int NF = C::NF;
   const int j0 = (logical % wg_per_head) * C::KEYS_PER_WG;
 
-  // this wave's two key fragments -> registers (B operand layout)
+  // this wave's key fragments -> registers (B operand layout)
   bf16x8 bk[NF][C::KS];
   int key[NF];
 #pragma unroll
@@ -187,18 +190,43 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
   }
 }
 
-template <int D>
-hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
-                           const float* lse, float* scores, const ScoreShape& s,
-                           hipStream_t stream) {
-  const int wg_per_head = (s.n_c + ColCfg<D>::KEYS_PER_WG - 1) / ColCfg<D>::KEYS_PER_WG;
+template <int D, int NF>
+hipError_t launch_colmax_nf(const uint16_t* q, const uint16_t* k_ctx,
+                            const float* lse, float* scores, const ScoreShape& s,
+                            hipStream_t stream) {
+  constexpr int KPW = ColCfg<D, NF>::KEYS_PER_WG;
+  const int wg_per_head = (s.n_c + KPW - 1) / KPW;
   const long long grid = (long long)s.nheads * wg_per_head;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
   const float inv_scale = (float)(1.0 / (double)s.scale);
-  hipLaunchKernelGGL(colmax_kernel<D>, dim3((unsigned)grid), dim3(256), 0,
+  hipLaunchKernelGGL((colmax_kernel<D, NF>), dim3((unsigned)grid), dim3(256), 0,
                      stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
   return hipGetLastError();
+}
+
+// Key fragments per wave for n_c cached keys per work item at d <= 128:
+// three, unless padding the last workgroup of a work item to 384 keys would
+// waste more than 1/16 of the matrix work while 256-key workgroups waste
+// less (a chunk of 2048 keys: 11 % padded with three, none with two).  Four
+// fragments (512 keys) would spill registers at d = 128.
+int colmax_fragments(int n_c) {
+  const long long pad3 = (long long)(n_c + 383) / 384 * 384 - n_c;
+  const long long pad2 = (long long)(n_c + 255) / 256 * 256 - n_c;
+  return (pad3 * 16 > (long long)n_c + pad3 && pad2 < pad3) ? 2 : 3;
+}
+
+template <int D>
+hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
+                           const float* lse, float* scores, const ScoreShape& s,
+                           hipStream_t stream) {
+  if constexpr (D == 256) {
+    return launch_colmax_nf<D, 2>(q, k_ctx, lse, scores, s, stream);
+  } else {
+    if (colmax_fragments(s.n_c) == 2)
+      return launch_colmax_nf<D, 2>(q, k_ctx, lse, scores, s, stream);
+    return launch_colmax_nf<D, 3>(q, k_ctx, lse, scores, s, stream);
+  }
 }
 
 }  // namespace
