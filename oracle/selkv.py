@@ -24,6 +24,11 @@ Readings taken here:
     with every g = 0 this is plain eviction, with every g = 1 a uniform mean;
   - the merge mass sum_e g_e of every kept row is reported (the quantity a
     count-based compensation would use).
+
+Parity unpinned for the merged rows as the page's method: the merge formula
+is not on the page, so the pins of merge() check this reading (closed forms
+of the weighted mean, planted mistakes), not the page.  The gate itself is
+pinned against the page's definition.
 """
 from __future__ import annotations
 
