@@ -95,3 +95,40 @@ def test_epikv_path_graph_replay():
         kvq.kv_compact_tokens(kc, vc, idx, ko, vo, st)
 
     _replay_and_check(step, [g, sc, idx, ko, vo])
+
+
+def test_chunked_and_merge_graph_replay():
+    """Chunked scoring (two launches per pass: full chunks and the shorter
+    last one), the per-(l, h) budget and the gated merge with routing built
+    once on the host, captured as one step."""
+    w = synth.LLAMA8B_8K.shrink(L=2, H=2, n_c=2500, n_prompt=32)
+    chunk = 1024                       # chunks of 1024, 1024 and 452 keys
+    gen = synth.generate_chunked_workload(w, chunk, workers=1)
+    q, kc, kn, vc = (to_dev_bf16(gen[k]) for k in ("q", "k_ctx", "k_new", "v_ctx"))
+    scale = float(w.scale)
+    n_ch, rows = kvq.kv_chunk_layout(w.n_c, w.n_prompt, chunk)
+    lse = torch.empty((w.L, w.H, rows * w.G), dtype=torch.float32, device="cuda")
+    sc = torch.empty((w.L, w.H, w.n_c), dtype=torch.float32, device="cuda")
+    total = kvq.kv_topk_total(w.L, w.H, w.n_c, w.keep_ratio, 0)
+    off = torch.empty(w.L * w.H + 1, dtype=torch.int64, device="cuda")
+    idx = torch.empty(total, dtype=torch.int32, device="cuda")
+    # the kept set is deterministic: build the routing from one eager run
+    kvq.kvscore_chunked_lse(q, kc, kn, w.G, w.n_prompt, chunk, lse, scale)
+    kvq.kvscore_chunked_colmax(q, kc, lse, w.G, w.n_prompt, chunk, sc, scale)
+    kvq.kv_topk_select(sc, w.keep_ratio, 0, off, idx)
+    torch.cuda.synchronize()
+    so_np, si_np = synth.nearest_position_routes(off.cpu().numpy(), idx.cpu().numpy(), w.n_c)
+    so, si = torch.from_numpy(so_np).cuda(), torch.from_numpy(si_np).cuda()
+    ko = torch.empty((total, w.d), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    gate = torch.empty(si.numel(), dtype=torch.float32, device="cuda")
+    mass = torch.empty(total, dtype=torch.float32, device="cuda")
+
+    def step():
+        st = torch.cuda.current_stream()
+        kvq.kvscore_chunked_lse(q, kc, kn, w.G, w.n_prompt, chunk, lse, scale, st)
+        kvq.kvscore_chunked_colmax(q, kc, lse, w.G, w.n_prompt, chunk, sc, scale, st)
+        kvq.kv_topk_select(sc, w.keep_ratio, 0, off, idx, st)
+        kvq.kv_merge_compact(kc, vc, off, idx, so, si, ko, vo, gate, mass, st)
+
+    _replay_and_check(step, [lse, sc, off, idx, ko, vo, gate, mass])

@@ -58,3 +58,46 @@ def test_two_streams_match_sequential():
             assert torch.equal(x, y), (rep, "a", i)
         for i, (x, y) in enumerate(zip(seq_b, par_b)):
             assert torch.equal(x, y), (rep, "b", i)
+
+
+def _chunked_path(dev, w, chunk, routes, stream):
+    """Chunked scoring, per-(l, h) budget and the gated merge on `stream`."""
+    with torch.cuda.stream(stream):
+        scores, lse = kvq.score_chunked(dev["q"], dev["k_ctx"], dev["k_new"], w.G,
+                                        w.n_prompt, chunk, stream=stream)
+        off, idx = kvq.kv_topk_select(scores, w.keep_ratio, 0, stream=stream)
+        so, si = routes
+        ko, vo, gate, mass = kvq.kv_merge_compact(dev["k_ctx"], dev["v_ctx"], off, idx, so, si,
+                                                  stream=stream)
+    return [lse, scores, off, idx, ko, vo, gate, mass]
+
+
+def test_two_streams_chunked_and_merge():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    print("two-stream reentrancy: chunked scoring and gated merge", flush=True)
+    wa = synth.LLAMA8B_8K.shrink(L=2, H=2, n_c=2500, n_prompt=32, seed=21)
+    wb = synth.LLAMA8B_8K.shrink(L=1, H=3, n_c=1800, n_prompt=7, G=2, d=64, rank=4, seed=22)
+    ca, cb = 1024, 512
+    da = {k: to_dev_bf16(v) for k, v in synth.generate_chunked_workload(wa, ca, workers=1).items()}
+    db = {k: to_dev_bf16(v) for k, v in synth.generate_chunked_workload(wb, cb, workers=1).items()}
+    s0 = torch.cuda.current_stream()
+    routes = []
+    for d_, w_, c_ in ((da, wa, ca), (db, wb, cb)):   # routing from the (deterministic) kept set
+        sc, _ = kvq.score_chunked(d_["q"], d_["k_ctx"], d_["k_new"], w_.G, w_.n_prompt, c_)
+        off, idx = kvq.kv_topk_select(sc, w_.keep_ratio, 0)
+        so, si = synth.nearest_position_routes(off.cpu().numpy(), idx.cpu().numpy(), w_.n_c)
+        routes.append((torch.from_numpy(so).cuda(), torch.from_numpy(si).cuda()))
+    seq_a = [t.clone() for t in _chunked_path(da, wa, ca, routes[0], s0)]
+    seq_b = [t.clone() for t in _chunked_path(db, wb, cb, routes[1], s0)]
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(s0)
+    sb.wait_stream(s0)
+    for rep in range(3):
+        par_a = _chunked_path(da, wa, ca, routes[0], sa)
+        par_b = _chunked_path(db, wb, cb, routes[1], sb)
+        torch.cuda.synchronize()
+        for i, (x, y) in enumerate(zip(seq_a, par_a)):
+            assert torch.equal(x, y), (rep, "a", i)
+        for i, (x, y) in enumerate(zip(seq_b, par_b)):
+            assert torch.equal(x, y), (rep, "b", i)
