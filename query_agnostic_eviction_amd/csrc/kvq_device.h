@@ -103,6 +103,22 @@ struct Tile {
     const int c = 2 * s + (lane >> 5);
     return r * D + ((c ^ swz(r)) * 8);
   }
+  // The same offset from two per-lane values, so that no table of KS offsets
+  // stays live: with chunk c = 2 s + h (h = lane / 32) and any swizzle value
+  // w, c ^ w = 2 (s ^ (w >> 1)) + (h ^ (w & 1)), hence
+  //   read_off(lane, s) = read_base(lane) + 16 * (s ^ read_x(lane)).
+  __device__ static __forceinline__ int read_base(int lane) {
+    const int r = lane & 31;
+    return r * D + 8 * ((lane >> 5) ^ (swz(r) & 1));
+  }
+  __device__ static __forceinline__ int read_x(int lane) { return swz(lane & 31) >> 1; }
+  // src_rel(i, tid) = src_rel(i & 1, tid) + (i & ~1) * 2048: one slot is 256
+  // chunks = 2048 elements, and two slots span 4096 / D >= 16 rows, a whole
+  // number of swizzle periods (16 rows), so two per-thread offsets serve
+  // every load of a tile.
+  __device__ static __forceinline__ int src_rel_from(const int (&rel01)[2], int i) {
+    return rel01[i & 1] + (i & ~1) * 2048;
+  }
 };
 
 // 16-byte global -> LDS copy; `lds` must be the same for the whole wave (the

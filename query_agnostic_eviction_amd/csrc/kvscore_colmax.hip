@@ -10,18 +10,21 @@
 // monotone, max_i exp(t_i) = exp(max_i t_i): no per-logit exp is needed.
 //
 // Mapping on gfx950:
-//  * A workgroup of 4 waves owns 384 cached keys (3 fragments of 32 per
+//  * A workgroup of 4 waves owns 512 cached keys (4 fragments of 32 per
 //    wave, kept in registers as the B operand; 256 keys in 2 fragments at
-//    d = 256, so that two waves fit per SIMD, and where 384-key workgroups
-//    would leave much padding); it sweeps all G * n_in query
-//    rows of its head in 32 KB tiles (16384 / d rows), double-buffered and
-//    filled by LDS-DMA straight from HBM together with the rows' lse.
+//    d = 256, where a fragment takes twice the registers); it sweeps all
+//    G * n_in query rows of its head in 32 KB tiles (16384 / d rows),
+//    double-buffered and filled by LDS-DMA straight from HBM together with
+//    the rows' lse.  Every operand read from LDS feeds four matrix ops.
 //  * The accumulator of each 32x32x16 product is seeded with -lse / scale of
 //    its rows, so the matrix op itself yields q.k - lse / scale; each lane
-//    holds 16 rows of one key and keeps a lane-local running max.
-//  * Each operand read from LDS feeds three matrix ops; the reductions are
-//    max3 on the accumulators (built without NaN semantics, so no
-//    canonicalising copies: inputs are finite and -inf marks padding).
+//    holds 16 rows of one key and keeps a lane-local running max (max3 on
+//    the accumulators, built without NaN semantics: inputs are finite).
+//  * Rows are never masked: the last tile is shifted back to end at the last
+//    row, and rows it shares with the tile before are simply seen twice,
+//    which leaves a maximum unchanged.  Together with per-lane operand
+//    offsets formed on the fly this keeps four fragments per wave within
+//    the registers of two waves per SIMD.
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
@@ -30,47 +33,46 @@
 namespace kvq {
 namespace {
 
-// NF_: cached-key fragments of 32 per wave; each operand read from LDS feeds
-// NF_ matrix ops.  Three by default; two at d = 256, so that two waves fit
-// per SIMD, and also where three would leave much of the last workgroup of
-// each work item padding (see colmax_fragments).
-template <int D, int NF_>
+template <int D>
 struct ColCfg {
   static constexpr int QT = Tile<D>::ROWS;  // query rows per tile
   static constexpr int NSUB = QT / 32;
   static constexpr int KS = D / 16;
   static constexpr int LSE_LOADS = QT / 64;  // 4-byte DMA instructions per tile
-  static constexpr int NF = NF_;
+  // cached-key fragments of 32 per wave: each operand read from LDS feeds
+  // NF matrix ops
+  static constexpr int NF = D == 256 ? 2 : 4;
   static constexpr int KEYS_PER_WG = 4 * NF * 32;
 };
 
-template <int D, int NF_>
+// SMALL: fewer rows than one tile (G * n_in < QT); the tile then clamps rows
+// past the last one to the last row (duplicates again).
+template <int D, bool SMALL>
 __global__ __launch_bounds__(256, 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const float* __restrict__ lse, float* __restrict__ scores,
     const ScoreShape sh, int wg_per_head, float c2, float inv_scale) {
-  const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
-  using C = ColCfg<D, NF_>;
+  using C = ColCfg<D>;
   using TL = Tile<D>;
+  constexpr int NF = C::NF;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[2 * TL::ELEMS];
   __shared__ __attribute__((aligned(1024))) float sl[2 * C::QT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int u = logical / wg_per_head;  // work item: (layer, KV head[, chunk])
-  constexpr int NF = C::NF;
   const int j0 = (logical % wg_per_head) * C::KEYS_PER_WG;
 
   // this wave's key fragments -> registers (B operand layout)
   bf16x8 bk[NF][C::KS];
-  int key[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    key[f] = j0 + 32 * (NF * wave + f) + (lane & 31);
-    const bool ok = key[f] < n_c;
-    const uint16_t* src =
-        k_ctx + map_offset(sh.k_ctx, u, sh.inner) + (size_t)(ok ? key[f] : 0) * D +
-        8 * (lane >> 5);
+    const int key = j0 + 32 * (NF * wave + f) + (lane & 31);
+    const bool ok = key < n_c;
+    const uint16_t* src = k_ctx + map_offset(sh.k_ctx, u, sh.inner) +
+                          (size_t)(ok ? key : 0) * D + 8 * (lane >> 5);
     const uint32_t keep = ok ? 0xffffffffu : 0u;  // keys past n_c read as zeros
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) bk[f][s] = as_bf16x8(ldg16(src + 16 * s) & keep);
@@ -81,35 +83,32 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
   const float* lh_lse = lse + map_offset(sh.lse, u, sh.inner);
   const int T = (R + C::QT - 1) / C::QT;
 
-  int src_rel[TL::LOADS];
-#pragma unroll
-  for (int i = 0; i < TL::LOADS; ++i) src_rel[i] = TL::src_rel(i, tid);
-  int rd_off[C::KS];
-#pragma unroll
-  for (int s = 0; s < C::KS; ++s) rd_off[s] = TL::read_off(lane, s);
+  const int rel01[2] = {TL::src_rel(0, tid), TL::src_rel(1, tid)};
+  const int rd_base = TL::read_base(lane), rd_x = TL::read_x(lane);
 
-  // LDS-DMA of tile t (query rows and their lse) into buffer `buf`; rows
-  // past R re-read row R-1 (finite values; their seed is -inf)
+  // LDS-DMA of tile t (query rows and their lse) into buffer `buf`.  The
+  // last tile starts at R - QT, so every load is in bounds.
   auto issue_tile = [&](int t, int buf) {
-    const int r0 = t * C::QT;
+    const int r0 = SMALL ? 0 : min(t * C::QT, R - C::QT);
     const uint16_t* base = qh + (size_t)r0 * D;
     uint16_t* dst = sq + buf * TL::ELEMS + wave * 64 * 8;
-    if (r0 + C::QT <= R) {
+    if constexpr (!SMALL) {
 #pragma unroll
-      for (int i = 0; i < TL::LOADS; ++i) lds_dma16(base + src_rel[i], dst + i * 256 * 8);
+      for (int i = 0; i < TL::LOADS; ++i)
+        lds_dma16(base + TL::src_rel_from(rel01, i), dst + i * 256 * 8);
       if (wave < C::LSE_LOADS)
         lds_dma4(lh_lse + r0 + wave * 64 + lane, sl + buf * C::QT + wave * 64);
     } else {
-      const int last = R - 1 - r0;
+      const int last = R - 1;
 #pragma unroll
       for (int i = 0; i < TL::LOADS; ++i) {
         const int r = TL::src_row(i, tid);
-        const int rel = src_rel[i] - (r > last ? (r - last) * D : 0);
+        const int rel = TL::src_rel_from(rel01, i) - (r > last ? (r - last) * D : 0);
         lds_dma16(base + rel, dst + i * 256 * 8);
       }
       if (wave < C::LSE_LOADS) {
         const int r = wave * 64 + lane;
-        lds_dma4(lh_lse + r0 + (r > last ? last : r), sl + buf * C::QT + wave * 64);
+        lds_dma4(lh_lse + (r > last ? last : r), sl + buf * C::QT + wave * 64);
       }
     }
   };
@@ -117,17 +116,10 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
   float M[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) M[f] = -__builtin_inff();
-  auto reduceN = [&](const f32x16* x) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        M[f] = max3f(M[f], x[f][4 * u], max3f(x[f][4 * u + 1], x[f][4 * u + 2], x[f][4 * u + 3]));
-  };
 
-  // one 32-row subtile: seed with -lse/scale of the lane's 16 rows (-inf
-  // for rows past R), run the products, fold them into the running maxima
-  auto subtile = [&](const uint16_t* sb, const float* slb, bool partial, int rbase) {
+  // one 32-row subtile: seed with -lse/scale of the lane's 16 rows, run the
+  // products, fold them into the running maxima
+  auto subtile = [&](const uint16_t* sb, const float* slb) {
     f32x16 init;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -135,39 +127,31 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) init[4 * grp + e] = -v[e] * inv_scale;
     }
-    if (partial) {
-      const int lim = R - 1 - rbase - 4 * (lane >> 5);
-#pragma unroll
-      for (int a = 0; a < 16; ++a)
-        if ((8 * (a >> 2) + (a & 3)) > lim) init[a] = -__builtin_inff();
-    }
     f32x16 c[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) c[f] = init;
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
 #pragma unroll
       for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], c[f]);
     }
-    reduceN(c);
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        M[f] = max3f(M[f], c[f][4 * g4], max3f(c[f][4 * g4 + 1], c[f][4 * g4 + 2], c[f][4 * g4 + 3]));
   };
 
+  // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
+  // t, then wait for the prefetch and publish it with one barrier
   auto step = [&](int t, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     if (t + 1 < T) issue_tile(t + 1, BUF ^ 1);
-    const int r0 = t * C::QT;
     const uint16_t* sb = sq + BUF * TL::ELEMS;
     const float* slb = sl + BUF * C::QT;
-    if (r0 + C::QT <= R) {
 #pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, slb + sub * 32, false, r0 + sub * 32);
-    } else {
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, slb + sub * 32, true, r0 + sub * 32);
-    }
+    for (int sub = 0; sub < C::NSUB; ++sub) subtile(sb + sub * 32 * D, slb + sub * 32);
     wait_all_mem();
     __syncthreads();
   };
@@ -185,48 +169,30 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
     const float mx = __builtin_fmaxf(M[f], __shfl_xor(M[f], 32));
     // the exact score is a probability, so never above 1
     const float sc = __builtin_fminf(fast_exp2(mx * c2), 1.0f);
-    if (lane < 32 && key[f] < n_c)
-      scores[map_offset(sh.scores, u, sh.inner) + key[f]] = sc;
+    const int key = j0 + 32 * (NF * wave + f) + (lane & 31);
+    if (lane < 32 && key < n_c) scores[map_offset(sh.scores, u, sh.inner) + key] = sc;
   }
-}
-
-template <int D, int NF>
-hipError_t launch_colmax_nf(const uint16_t* q, const uint16_t* k_ctx,
-                            const float* lse, float* scores, const ScoreShape& s,
-                            hipStream_t stream) {
-  constexpr int KPW = ColCfg<D, NF>::KEYS_PER_WG;
-  const int wg_per_head = (s.n_c + KPW - 1) / KPW;
-  const long long grid = (long long)s.nheads * wg_per_head;
-  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const float c2 = s.scale * kLog2e;
-  const float inv_scale = (float)(1.0 / (double)s.scale);
-  hipLaunchKernelGGL((colmax_kernel<D, NF>), dim3((unsigned)grid), dim3(256), 0,
-                     stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
-  return hipGetLastError();
-}
-
-// Key fragments per wave for n_c cached keys per work item at d <= 128:
-// three, unless padding the last workgroup of a work item to 384 keys would
-// waste more than 1/16 of the matrix work while 256-key workgroups waste
-// less (a chunk of 2048 keys: 11 % padded with three, none with two).  Four
-// fragments (512 keys) would spill registers at d = 128.
-int colmax_fragments(int n_c) {
-  const long long pad3 = (long long)(n_c + 383) / 384 * 384 - n_c;
-  const long long pad2 = (long long)(n_c + 255) / 256 * 256 - n_c;
-  return (pad3 * 16 > (long long)n_c + pad3 && pad2 < pad3) ? 2 : 3;
 }
 
 template <int D>
 hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
                            const float* lse, float* scores, const ScoreShape& s,
                            hipStream_t stream) {
-  if constexpr (D == 256) {
-    return launch_colmax_nf<D, 2>(q, k_ctx, lse, scores, s, stream);
-  } else {
-    if (colmax_fragments(s.n_c) == 2)
-      return launch_colmax_nf<D, 2>(q, k_ctx, lse, scores, s, stream);
-    return launch_colmax_nf<D, 3>(q, k_ctx, lse, scores, s, stream);
-  }
+  constexpr int KPW = ColCfg<D>::KEYS_PER_WG;
+  // the last workgroup of a work item is padded (keys past n_c read as zeros
+  // and are not stored)
+  const int wg_per_head = (s.n_c + KPW - 1) / KPW;
+  const long long grid = (long long)s.nheads * wg_per_head;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float c2 = s.scale * kLog2e;
+  const float inv_scale = (float)(1.0 / (double)s.scale);
+  if ((long long)s.G * s.n_in < ColCfg<D>::QT)
+    hipLaunchKernelGGL((colmax_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
+  else
+    hipLaunchKernelGGL((colmax_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
+  return hipGetLastError();
 }
 
 }  // namespace
