@@ -6,11 +6,10 @@
 // lse[l][h][g][i] = ln sum_{seen j} exp(scale * <q_{g,i}, k_j>).
 //
 // Mapping on gfx950:
-//  * A workgroup of 4 waves owns 8 query fragments of 32 rows each (a
+//  * A workgroup of 4 waves owns 4 * NFQ query fragments of 32 rows each (a
 //    fragment is 32 consecutive positions of one query head g; fragments of
 //    a head are numbered b * G + g over 32-position blocks b).  Each wave
-//    keeps its two fragments' queries in registers for the whole key sweep,
-//    so every key operand read from LDS feeds two matrix ops.
+//    keeps its NFQ fragments' queries in registers for the whole key sweep.
 //  * Keys stream through LDS in 32 KB tiles (16384 / d keys), double-buffered
 //    and filled by LDS-DMA straight from HBM while the previous tile is in
 //    use: first the cached keys, then the new keys up to the workgroup's last
@@ -19,17 +18,28 @@
 //    A operand and the queries as B, so each lane holds 16 keys of one query:
 //    the softmax sums stay lane-local; the two half-waves that share a query
 //    merge once at the end.
+//  * d <= 128 (four fragments per wave): a 32-key subtile's key operands are
+//    read from LDS once into registers and feed the products of all four
+//    fragments, which are staggered: while the matrix core runs the chain of
+//    fragment f, the VALU reduces the logits of fragment f - 1 (for f = 0,
+//    the last fragment of the previous subtile).  Only two sets of
+//    accumulators are live, which is what leaves room for four fragments'
+//    queries (128 registers at d = 128).
+//  * d = 256 (two fragments per wave): a subtile's key operands would take
+//    64 registers, so each is read once and fed to both fragments at once;
+//    the subtile is reduced right after its own products and the other wave
+//    on the SIMD provides the overlap.
 //  * exp is taken as exp2 with the scale folded into one FMA per logit; the
-//    running max is updated lazily (see accumulate), so the hot path has no
-//    per-logit max, and masked keys enter as a -inf accumulator seed.
+//    running max is updated lazily (see reduce), so the hot path has no
+//    per-logit max.  Logits of keys a row must not see are set to -inf after
+//    the products of the few subtiles that hold such keys (under a uniform
+//    branch; the paired schedule seeds its accumulators instead).
 //  * Subtile sums enter each lane's running sum with Kahan compensation
 //    (per subtile, not per logit), so 128K-key rows stay at fp32 accuracy.
-//  * The loop is software-pipelined by one 32-key subtile so the matrix
-//    cores and the VALU/transcendental units work at the same time.  At
-//    d = 256 the second set of accumulators would not fit beside two
-//    fragments' queries at two waves per SIMD, so there each subtile is
-//    reduced right after its own matrix ops (the other wave on the SIMD
-//    provides the overlap).
+//  * With the staggered schedule a wave stops computing after the last tile
+//    holding a key its rows see (and a wave holding no rows computes
+//    nothing); it keeps issuing its share of the tile loads and joining the
+//    barriers.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -43,12 +53,11 @@ struct LseCfg {
   static constexpr int KT = Tile<D>::ROWS;  // keys per tile
   static constexpr int NSUB = KT / 32;      // 32-key subtiles per tile
   static constexpr int KS = D / 16;         // k-steps of the 32x32x16 op
-  // query fragments per wave: two share each key operand read
-  static constexpr int NFQ = 2;
-  // one-subtile software pipeline (a second set of accumulators); off at
-  // d = 256, where it would not fit at two waves per SIMD
-  static constexpr bool PIPE = D != 256;
+  // query fragments per wave: each key operand read feeds NFQ matrix ops
+  static constexpr int NFQ = D == 256 ? 2 : 4;
   static constexpr int FPW = 4 * NFQ;      // fragments per workgroup
+  // staggered fragments (key operands of a subtile held in registers)
+  static constexpr bool STAGGER = D != 256;
 };
 
 template <int D>
@@ -57,64 +66,101 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     const uint16_t* __restrict__ k_new, float* __restrict__ lse,
     const ScoreShape sh, int nfrag_head, int wg_per_head, float c2) {
   using C = LseCfg<D>;
+  using TL = Tile<D>;
+  constexpr int NFQ = C::NFQ;
   const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
   const float scale = sh.scale;
-  using TL = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t sk[2 * TL::ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int u = logical / wg_per_head;  // work item: (layer, KV head[, chunk])
   // latest positions (most keys) first
   const int wgi = wg_per_head - 1 - logical % wg_per_head;
 
-  constexpr int NFQ = C::NFQ;
-  // fragment bookkeeping (uniform per wave)
+  // workgroup bookkeeping: its first position and how far its new keys go
   const int F_first = C::FPW * wgi;
   const int F_last = min(C::FPW * wgi + C::FPW - 1, nfrag_head - 1);
   const int pos_min = 32 * (F_first / G);
   const int new_len = min(n_in, 32 * (F_last / G + 1));
 
+  // the wave's fragments (uniform per wave)
   int fg[NFQ], fpos0[NFQ];
   bool fvalid[NFQ];
+  int wave_last = -1;  // last position a row of this wave holds (-1: none)
 #pragma unroll
   for (int f = 0; f < NFQ; ++f) {
     const int F = C::FPW * wgi + NFQ * wave + f;
     fvalid[f] = F < nfrag_head;
     fg[f] = fvalid[f] ? F % G : 0;
     fpos0[f] = fvalid[f] ? 32 * (F / G) : 0;
+    if (fvalid[f]) wave_last = max(wave_last, min(fpos0[f] + 31, n_in - 1));
   }
 
-  // queries of the wave's fragments -> registers (B operand layout)
-  bf16x8 bq[NFQ][C::KS];
-#pragma unroll
-  for (int f = 0; f < NFQ; ++f) {
+  // queries of the wave's fragments -> registers (B operand layout); one
+  // array per fragment.  (Every helper below is forced inline: a helper left
+  // out of line would keep these arrays in scratch memory.)
+  bf16x8 bq0[C::KS], bq1[C::KS], bq2[C::KS], bq3[C::KS];
+  auto load_q = [&](bf16x8 (&dst)[C::KS], int f) __attribute__((always_inline)) {
     const int pos = fpos0[f] + (lane & 31);
     const bool ok = fvalid[f] && pos < n_in;
     const uint16_t* src = q + map_offset(sh.q, u, sh.inner) +
                           ((size_t)fg[f] * n_in + (ok ? pos : 0)) * D + 8 * (lane >> 5);
     const uint32_t keep = ok ? 0xffffffffu : 0u;  // padding rows read as zeros
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) bq[f][s] = as_bf16x8(ldg16(src + 16 * s) & keep);
-  }
+    for (int s = 0; s < C::KS; ++s) dst[s] = as_bf16x8(ldg16(src + 16 * s) & keep);
+  };
+  load_q(bq0, 0);
+  if constexpr (NFQ > 1) load_q(bq1, 1);
+  if constexpr (NFQ > 2) load_q(bq2, 2);
+  if constexpr (NFQ > 3) load_q(bq3, 3);
+  auto qop = [&](auto f_tag, int s) __attribute__((always_inline)) -> const bf16x8& {
+    constexpr int f = decltype(f_tag)::value;
+    if constexpr (f == 0) return bq0[s];
+    else if constexpr (f == 1) return bq1[s];
+    else if constexpr (f == 2) return bq2[s];
+    else return bq3[s];
+  };
 
   const uint16_t* seg_ptr[2] = {k_ctx + map_offset(sh.k_ctx, u, sh.inner),
                                 k_new + map_offset(sh.k_new, u, sh.inner)};
   const int T0 = (n_c + C::KT - 1) / C::KT;
   const int T1 = (new_len + C::KT - 1) / C::KT;
   const int T = T0 + T1;
+  // tiles this wave computes on: with the staggered schedule every
+  // cached-key tile and the new-key tiles up to its last position; the
+  // paired schedule sweeps the workgroup's tiles
+  const int Tw = !C::STAGGER ? T : (wave_last < 0 ? 0 : T0 + (wave_last + C::KT) / C::KT);
 
-  // per-thread constant parts of the tile loads and of the operand reads
-  int src_rel[TL::LOADS];
+  // Per-thread parts of the tile-load and key-operand addresses.  The
+  // staggered schedule has no registers to spare: two values each, combined
+  // on the fly.  The paired schedule reads a key operand per product pair,
+  // so there a table per load slot and per k-step keeps that arithmetic off
+  // the reads.
+  const int rel01[2] = {TL::src_rel(0, tid), TL::src_rel(1, tid)};
+  const int rd_base = TL::read_base(lane), rd_x = TL::read_x(lane);
+  int rel_t[C::STAGGER ? 1 : TL::LOADS], rd_t[C::STAGGER ? 1 : C::KS];
+  if constexpr (!C::STAGGER) {
 #pragma unroll
-  for (int i = 0; i < TL::LOADS; ++i) src_rel[i] = TL::src_rel(i, tid);
-  int rd_off[C::KS];
+    for (int i = 0; i < TL::LOADS; ++i) rel_t[i] = TL::src_rel(i, tid);
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s) rd_off[s] = TL::read_off(lane, s);
+    for (int s = 0; s < C::KS; ++s) rd_t[s] = TL::read_off(lane, s);
+  }
+  auto load_rel = [&](int i) __attribute__((always_inline)) {
+    if constexpr (C::STAGGER) return TL::src_rel_from(rel01, i);
+    else return rel_t[i];
+  };
+  auto key_op = [&](const uint16_t* sb, int s) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (C::STAGGER)
+      return *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
+    else
+      return *reinterpret_cast<const bf16x8*>(sb + rd_t[s]);
+  };
 
   // LDS-DMA of tile t into buffer `buf`; rows past the segment end re-read
-  // its last row (finite values; those keys are masked by the -inf seed)
-  auto issue_tile = [&](int t, int buf) {
+  // its last row (finite values; those keys are masked)
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
     const int seg = t < T0 ? 0 : 1;
     const int key0 = (seg == 0 ? t : t - T0) * C::KT;
     const int len = seg == 0 ? n_c : new_len;
@@ -122,13 +168,14 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     uint16_t* dst = sk + buf * TL::ELEMS + wave * 64 * 8;
     if (key0 + C::KT <= len) {
 #pragma unroll
-      for (int i = 0; i < TL::LOADS; ++i) lds_dma16(base + src_rel[i], dst + i * 256 * 8);
+      for (int i = 0; i < TL::LOADS; ++i)
+        lds_dma16(base + load_rel(i), dst + i * 256 * 8);
     } else {
       const int last = len - 1 - key0;
 #pragma unroll
       for (int i = 0; i < TL::LOADS; ++i) {
         const int r = TL::src_row(i, tid);
-        const int rel = src_rel[i] - (r > last ? (r - last) * D : 0);
+        const int rel = load_rel(i) - (r > last ? (r - last) * D : 0);
         lds_dma16(base + rel, dst + i * 256 * 8);
       }
     }
@@ -142,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // stay far from overflow (< 2^64 per subtile) and terms far below m only
   // underflow where they are negligible, so the result is exact to fp32
   // rounding while the hot path costs one FMA, one exp2 and one add per logit.
-  float m[NFQ], nmc[NFQ];
+  float m[NFQ];
   // running sums with a compensation term (Kahan): long contexts add
   // thousands of subtile sums of similar size, whose rounding errors would
   // otherwise accumulate
@@ -150,51 +197,68 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
 #pragma unroll
   for (int f = 0; f < NFQ; ++f) {
     m[f] = kNegBig;
-    nmc[f] = -kNegBig * c2;
     sum[f] = comp[f] = 0.f;
   }
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
 
-  auto accumulate = [&](const f32x16* x) {
-    // four running partial sums per fragment keep few temporaries live
-    float e[NFQ][4];
+  // fold one fragment's 16 logits per lane (a subtile) into its running sum
+  auto reduce = [&](const f32x16& x, auto f_tag) __attribute__((always_inline)) {
+    constexpr int f = decltype(f_tag)::value;
+    float nmc = -m[f] * c2;
+    // four running partial sums keep few temporaries live
+    float e[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) e[a] = fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+#pragma unroll
+    for (int a = 4; a < 16; ++a) e[a & 3] += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+    float ts = (e[0] + e[1]) + (e[2] + e[3]);
+    if (!(ts <= kRescaleAt)) {
+      // rare path: raise the running max to this subtile's max and re-sum
+      float tm = x[0];
+#pragma unroll
+      for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
+      const float mn = __builtin_fmaxf(m[f], tm);
+      const float rescale = fast_exp2((m[f] - mn) * c2);
+      sum[f] *= rescale;
+      comp[f] *= rescale;
+      m[f] = mn;
+      nmc = -mn * c2;
+      float t = 0.f;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+      ts = t;
+    }
+    const float y = ts - comp[f];
+    const float t = sum[f] + y;
+    comp[f] = (t - sum[f]) - y;
+    sum[f] = t;
+  };
+
+  // both fragments of the paired schedule at once: their exps interleave and
+  // one test covers the rare path of either
+  auto reduce_pair = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
+    const float nmc[2] = {-m[0] * c2, -m[1] * c2};
+    float e[2][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int f = 0; f < NFQ; ++f) e[f][a] = fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
+      for (int f = 0; f < 2; ++f) e[f][a] = fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
 #pragma unroll
     for (int a = 4; a < 16; ++a)
 #pragma unroll
-      for (int f = 0; f < NFQ; ++f) e[f][a & 3] += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
-    float ts[NFQ];
-    bool big = false;
+      for (int f = 0; f < 2; ++f) e[f][a & 3] += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
+    float ts[2];
 #pragma unroll
-    for (int f = 0; f < NFQ; ++f) {
-      ts[f] = (e[f][0] + e[f][1]) + (e[f][2] + e[f][3]);
-      big = big || !(ts[f] <= kRescaleAt);
-    }
-    if (big) {
-      // rare path: raise the running max to this subtile's max and re-sum
-#pragma unroll
-      for (int f = 0; f < NFQ; ++f) {
-        if (ts[f] <= kRescaleAt) continue;
-        float tm = x[f][0];
-#pragma unroll
-        for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[f][a]);
-        const float mn = __builtin_fmaxf(m[f], tm);
-        const float rescale = fast_exp2((m[f] - mn) * c2);
-        sum[f] *= rescale;
-        comp[f] *= rescale;
-        m[f] = mn;
-        nmc[f] = -mn * c2;
-        float t = 0.f;
-#pragma unroll
-        for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
-        ts[f] = t;
-      }
+    for (int f = 0; f < 2; ++f) ts[f] = (e[f][0] + e[f][1]) + (e[f][2] + e[f][3]);
+    if (!(ts[0] <= kRescaleAt) || !(ts[1] <= kRescaleAt)) {
+      // rare path: redo with the per-fragment reduction, which raises the
+      // running max of whichever fragment needs it
+      reduce(x[0], std::integral_constant<int, 0>{});
+      reduce(x[1], std::integral_constant<int, 1>{});
+      return;
     }
 #pragma unroll
-    for (int f = 0; f < NFQ; ++f) {
+    for (int f = 0; f < 2; ++f) {
       const float y = ts[f] - comp[f];
       const float t = sum[f] + y;
       comp[f] = (t - sum[f]) - y;
@@ -202,57 +266,69 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     }
   };
 
-  // Accumulator seed: 0 for keys a row sees, -inf for keys it must not see
-  // (cached-key tail past n_c, new keys past the row's position or past n_in).
-  auto seed = [&](int f, int seg, int kbase) {
-    f32x16 init;
+  // Masking: logits of keys a row must not see (cached-key tail past n_c, new
+  // keys past the row's position or past n_in) become -inf, which the
+  // reduction turns into 0.
+  auto mask = [&](f32x16& x, int f, int seg, int kbase) __attribute__((always_inline)) {
     // last key this lane's row may see within the segment
     const int qpos = fpos0[f] + (lane & 31);
     const int lim = (seg == 0 ? n_c - 1 : min(qpos, n_in - 1)) - kbase - 4 * (lane >> 5);
 #pragma unroll
     for (int a = 0; a < 16; ++a)
-      init[a] = (8 * (a >> 2) + (a & 3)) <= lim ? 0.f : -__builtin_inff();
-    return init;
+      if ((8 * (a >> 2) + (a & 3)) > lim) x[a] = -__builtin_inff();
   };
 
-  // software pipeline: the MFMAs of one 32-key subtile run while the VALU
-  // reduces the previous subtile's logits
-  f32x16 p[NFQ];
+  // staggered schedule: logits of the last fragment computed and not yet
+  // reduced (fragment NFQ-1 of the previous subtile when a subtile starts)
+  f32x16 pend;
 #pragma unroll
-  for (int f = 0; f < NFQ; ++f)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) p[f][a] = -__builtin_inff();
+  for (int a = 0; a < 16; ++a) pend[a] = -__builtin_inff();
 
-  // one 32-key subtile; unmasked subtiles start the chain from an inline zero
-  auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase) {
-    f32x16 c[NFQ];
+  // one 32-key subtile
+  auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase)
+                     __attribute__((always_inline)) {
+    if constexpr (C::STAGGER) {
+      bf16x8 ak[C::KS];
 #pragma unroll
-    for (int f = 0; f < NFQ; ++f) {
-      if (masked) {
-        c[f] = seed(f, seg, kbase);
-      } else {
+      for (int s = 0; s < C::KS; ++s) ak[s] = key_op(sb, s);
+      auto frag = [&](auto f_tag) __attribute__((always_inline)) {
+        constexpr int f = decltype(f_tag)::value;
+        f32x16 c = {};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) c = mfma32(ak[s], qop(f_tag, s), c);
+        reduce(pend, std::integral_constant<int, (f + NFQ - 1) % NFQ>{});
+        if (masked) mask(c, f, seg, kbase);
+        pend = c;
+        // keep the next fragment's work from being hoisted into this one
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      frag(std::integral_constant<int, 0>{});
+      if constexpr (NFQ > 1) frag(std::integral_constant<int, 1>{});
+      if constexpr (NFQ > 2) frag(std::integral_constant<int, 2>{});
+      if constexpr (NFQ > 3) frag(std::integral_constant<int, 3>{});
+    } else {
+      static_assert(NFQ == 2, "paired schedule holds two fragments");
+      // masked subtiles start from a -inf seed where a row must not see a key
+      f32x16 c[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
         const f32x16 z = {};
         c[f] = z;
+        if (masked) mask(c[f], f, seg, kbase);
       }
-    }
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_off[s]);
-#pragma unroll
-      for (int f = 0; f < NFQ; ++f) c[f] = mfma32(a, bq[f][s], c[f]);
-    }
-    if constexpr (C::PIPE) {
-      accumulate(p);
-#pragma unroll
-      for (int f = 0; f < NFQ; ++f) p[f] = c[f];
-    } else {
-      accumulate(c);
+      for (int s = 0; s < C::KS; ++s) {
+        const bf16x8 a = key_op(sb, s);
+        c[0] = mfma32(a, qop(std::integral_constant<int, 0>{}, s), c[0]);
+        c[1] = mfma32(a, qop(std::integral_constant<int, 1>{}, s), c[1]);
+      }
+      reduce_pair(c);
     }
   };
 
   // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
   // t, then wait for the prefetch and publish it with one barrier
-  auto step = [&](int t, auto buf_tag) {
+  auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     if (t + 1 < T) issue_tile(t + 1, BUF ^ 1);
     const int seg = t < T0 ? 0 : 1;
@@ -260,14 +336,15 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     const bool masked = seg == 0 ? (key0 + C::KT > n_c)
                                  : (key0 + C::KT - 1 > pos_min || key0 + C::KT > n_in);
     const uint16_t* sb = sk + BUF * TL::ELEMS;
-    if (masked) {
+    if (C::STAGGER || !masked) {
+      // (staggered: one copy, the mask applied under a uniform branch)
 #pragma unroll
       for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, true, seg, key0 + sub * 32);
+        subtile(sb + sub * 32 * D, C::STAGGER && masked, seg, key0 + sub * 32);
     } else {
 #pragma unroll
       for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, false, seg, key0 + sub * 32);
+        subtile(sb + sub * 32 * D, true, seg, key0 + sub * 32);
     }
     wait_all_mem();
     __syncthreads();
@@ -276,11 +353,22 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   issue_tile(0, 0);
   wait_all_mem();
   __syncthreads();
-  for (int t = 0; t < T; t += 2) {
+  int t = 0;
+  for (; t + 1 < Tw; t += 2) {
     step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < T) step(t + 1, std::integral_constant<int, 1>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
-  if constexpr (C::PIPE) accumulate(p);
+  if (t < Tw) {
+    step(t, std::integral_constant<int, 0>{});
+    ++t;
+  }
+  // tiles past this wave's rows: only its share of the loads and the barriers
+  for (; t < T; ++t) {
+    if (t + 1 < T) issue_tile(t + 1, (t & 1) ^ 1);
+    wait_all_mem();
+    __syncthreads();
+  }
+  if constexpr (C::STAGGER) reduce(pend, std::integral_constant<int, NFQ - 1>{});
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll
