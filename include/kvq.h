@@ -166,6 +166,21 @@ int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
                    int64_t capacity, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* kv_topk_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * same arguments, results and errors, without the workspace.  Mode 2 keeps
+ * its grid-wide state in a file-scope device array of 48 KiB (one per GPU,
+ * held until the process ends; every valid size needs at most ~33 KiB, and a
+ * larger need returns KV_ERR_CAPACITY).  Its address is looked up once per
+ * device on the first call there (hipGetSymbolAddress; a failure returns
+ * KV_ERR_HIP); the call itself allocates nothing.  Every call on one GPU
+ * shares that array, so calls that overlap on one GPU (for instance on two
+ * streams) race; calls ordered on one stream do not.  Modes 0 and 1 use no
+ * scratch. */
+int kv_topk_select_noalloc(const float* scores, int L, int H, int64_t n_c,
+                           double keep_ratio, int mode, int64_t* offsets,
+                           int32_t* idx, int64_t capacity, void* stream);
+
 /* Head-level static score (KVzip section 4.2, context-independent
  * eviction): head_scores[l][h] = max_j scores[l][h][j], the largest pair
  * score of each head along the sequence, as fp32 [L][H].  Exact (a max of

@@ -236,6 +236,24 @@ def kv_topk_select(scores: torch.Tensor, keep_ratio: float, mode: int = 0,
     return offsets, idx
 
 
+def kv_topk_select_noalloc(scores: torch.Tensor, keep_ratio: float, mode: int,
+                           offsets: torch.Tensor, idx: torch.Tensor,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kv_topk_select without a workspace and without allocating: the caller
+    passes the outputs; mode 2 uses the library's own per-GPU device array."""
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 3:
+        raise ValueError("scores must be [L,H,n_c]")
+    L, H, n_c = scores.shape
+    _dev(offsets, torch.int64, "offsets")
+    _dev(idx, torch.int32, "idx")
+    _size(offsets, L * H + 1, "offsets")
+    _check("kv_topk_select_noalloc", _lib.load().kv_topk_select_noalloc(
+        _ptr(scores), L, H, n_c, float(keep_ratio), mode, _ptr(offsets), _ptr(idx),
+        idx.numel(), _stream(stream)))
+    return offsets, idx
+
+
 def kv_head_scores(scores: torch.Tensor, out: Optional[torch.Tensor] = None,
                    stream=None) -> torch.Tensor:
     """Head-level static score (KVzip section 4.2): max of each head's scores."""

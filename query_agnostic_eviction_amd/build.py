@@ -64,7 +64,8 @@ DEVICE_HEADERS = ("kvq_device.h", "kvq_internal.h")
 # the source file that holds the kernels of each entry point
 KERNEL_SOURCES = {
     "kvscore_lse": "kvscore_lse.hip", "kvscore_colmax": "kvscore_colmax.hip",
-    "kv_topk_select": "kv_topk.hip", "kv_head_scores": "kv_topk.hip",
+    "kv_topk_select": "kv_topk.hip", "kv_topk_select_noalloc": "kv_topk.hip",
+    "kv_head_scores": "kv_topk.hip",
     "kv_select_tokens": "kv_topk.hip", "kv_compact": "kv_compact.hip",
     "kv_compact_tokens": "kv_compact.hip", "kv_epi_deltas": "epikv.hip",
     "kv_epi_scores": "epikv.hip", "kv_merge_compact": "selkv_merge.hip",

@@ -14,8 +14,17 @@
 //     equal to T, writing kept positions in ascending order through two
 //     block-wide prefix sums per chunk.
 // The result is unique (ties go to the lower index) and bit-exact.
+#include <mutex>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
+
+// Device memory of kv_topk_select_noalloc: the grid-wide select's state and
+// per-block counts (global_select_workspace bytes, at most ~33 KiB for any
+// input).  One copy per GPU, held until the process ends.  Host code must
+// never pass this name to a kernel or a copy: it is a host-side stand-in;
+// the device address comes from noalloc_scratch below.
+static __device__ __align__(256) unsigned char scratch[kvq::kNoAllocScratchBytes];
 
 namespace kvq {
 namespace {
@@ -521,6 +530,26 @@ hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nhe
 hipError_t launch_select_tokens_grid(const float* scores, long long n, long long k,
                                      int32_t* idx, void* workspace, hipStream_t stream) {
   return launch_global_select<true>(scores, n, n, 1, k, nullptr, idx, workspace, stream);
+}
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the address of this GPU's copy of the array (the current device's)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_head_max(const float* scores, int nheads, int n_c, float* out,

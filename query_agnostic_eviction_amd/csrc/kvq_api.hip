@@ -256,6 +256,30 @@ int kv_topk_select(const float* scores, int L, int H, int64_t n_c,
                                      idx, static_cast<hipStream_t>(stream)));
 }
 
+int kv_topk_select_noalloc(const float* scores, int L, int H, int64_t n_c,
+                           double keep_ratio, int mode, int64_t* offsets,
+                           int32_t* idx, int64_t capacity, void* stream) {
+  if (!scores || !offsets || !idx) return KV_ERR_INVALID_ARG;
+  int64_t total = 0;
+  int st = kv_topk_total(L, H, n_c, keep_ratio, mode, &total);
+  if (st != KV_OK) return st;
+  if (!aligned(scores, 4) || !aligned(offsets, 8) || !aligned(idx, 4))
+    return KV_ERR_ALIGNMENT;
+  if (capacity < total) return KV_ERR_CAPACITY;
+  const size_t ws_need = kv_topk_workspace_bytes(L, H, n_c, mode);
+  if (ws_need > kvq::kNoAllocScratchBytes) return KV_ERR_CAPACITY;
+  if (mode != 2)  // no scratch: the same launch as kv_topk_select
+    return kv_topk_select(scores, L, H, n_c, keep_ratio, mode, offsets, idx, capacity,
+                          nullptr, 0, stream);
+  void* ws = nullptr;
+  st = hip_status(kvq::noalloc_scratch(&ws));
+  if (st != KV_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_global_topk(scores, (int64_t)L * H * n_c, (int)n_c, L * H,
+                                            total, offsets, idx, ws,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
                    float* head_scores, void* stream) {
   if (!scores || !head_scores || L < 1 || H < 1 || n_c < 1) return KV_ERR_INVALID_ARG;

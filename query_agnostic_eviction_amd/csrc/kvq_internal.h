@@ -68,6 +68,11 @@ hipError_t launch_global_topk(const float* scores, long long n, int n_c, int nhe
                               long long k, int64_t* offsets, int32_t* idx,
                               void* workspace, hipStream_t stream);
 
+// Size of the file-scope device array behind kv_topk_select_noalloc, and the
+// current device's address of it (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = 48 * 1024;
+hipError_t noalloc_scratch(void** ptr);
+
 // Max of each head's scores.
 hipError_t launch_head_max(const float* scores, int nheads, int n_c, float* out,
                            hipStream_t stream);

@@ -156,6 +156,26 @@ def test_select_validation(lib):
     assert _sel(lib, sc=P2) == ALN
 
 
+def test_select_noalloc_validation(lib):
+    """The allocation-free selection rejects the same arguments as
+    kv_topk_select (minus the workspace ones) before touching a device."""
+    def sel(sc=P, L=2, H=2, n_c=100, r=0.3, mode=0, off=P, idx=P, cap=1000):
+        return lib.kv_topk_select_noalloc(sc, L, H, n_c, r, mode, off, idx, cap, NUL)
+    assert sel(sc=NUL) == INV
+    assert sel(off=NUL) == INV
+    assert sel(idx=NUL) == INV
+    for r in (0.0, 1.01, math.nan):
+        assert sel(r=r) == INV
+    assert sel(mode=3) == UNS
+    assert sel(n_c=0) == INV
+    assert sel(mode=2, cap=119) == CAP
+    assert sel(cap=4 * 30 - 1) == CAP
+    assert sel(off=P4) == ALN
+    assert sel(sc=P2) == ALN
+    # the largest mode-2 state fits the library's fixed device array
+    assert lib.kv_topk_workspace_bytes(1 << 9, 1 << 10, 1 << 21, 2) <= 48 * 1024
+
+
 def test_head_scores_validation(lib):
     f = lib.kv_head_scores
     assert f(NUL, 2, 2, 10, P, NUL) == INV
