@@ -179,7 +179,7 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None, merge=False):
     head_logits = w.G * (w.n_in * w.n_c + w.n_in * (w.n_in + 1) // 2)
     if not chunk and head_logits > 2e10:
         return cpu_baseline_rows(w, seconds, workers, head_logits)
-    done, t_oracle, heads = 0, 0.0, []
+    done, t_oracle, heads, ref = 0, 0.0, [], {}
     order = [(l, h) for l in range(w.L) for h in range(w.H)]
     for (l, h) in order:
         gen = synth.generate_chunked_head(w, l, h, chunk) if chunk else synth.generate_head(w, l, h)
@@ -201,6 +201,7 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None, merge=False):
         t_oracle += time.perf_counter() - t0
         done += w.n_c
         heads.append((l, h))
+        ref[(l, h)] = S
         if t_oracle >= seconds:
             break
     return {
@@ -214,6 +215,8 @@ def cpu_baseline(w, seconds: float, mode: int = 0, chunk=None, merge=False):
         "cpu_model": cpu_model(),
         # every head costs the same, so the whole workload would take this long
         "extrapolated_full_s": round(t_oracle / len(heads) * w.L * w.H, 1),
+        # the oracle's scores of those heads, for the accuracy fields (not printed)
+        "_ref_scores": ref,
     }
 
 
@@ -244,6 +247,47 @@ def cpu_baseline_rows(w, seconds, workers, head_logits):
         "cpu_model": cpu_model(),
         "extrapolated_full_s": round(t_head * w.L * w.H, 1),
     }
+
+
+SCORE_RTOL, SCORE_ATOL = 2e-3, 1e-6   # score tolerance against the oracle
+
+
+def accuracy_fields(ref, scores_gpu, offsets, idx, keep_ratio, mode):
+    """Per-run accuracy of the GPU scores on the heads the CPU baseline ran:
+    the largest relative score error, whether every score is within
+    |s - S| <= atol + rtol * S, and (per-head budget) the near-tie band: with
+    tau the k-th largest oracle score of a head, the keys with
+    (tau (1 - rtol) - 2 atol) / (1 + rtol) <= S <= (tau (1 + rtol) + 2 atol) / (1 - rtol)
+    could swap places within the tolerance; every key above the band must be
+    kept and every key below it dropped.  Plain arithmetic on the stored
+    oracle scores and the GPU outputs."""
+    import math
+    if not ref:
+        return {"max_rel_err": None, "scores_within_tol": None, "near_tie_band": None,
+                "topk_outside_band_ok": None, "heads_checked": 0}
+    H = scores_gpu.shape[1]
+    max_rel, ok, band_pop, sel_ok = 0.0, True, 0, True
+    for (l, h), S in ref.items():
+        g = scores_gpu[l, h].astype(np.float64)
+        err = np.abs(g - S)
+        max_rel = max(max_rel, float(np.max(err / S)))
+        ok = ok and bool(np.all(err <= SCORE_ATOL + SCORE_RTOL * S))
+        if mode == 0:
+            n = S.size
+            k = min(max(math.floor(keep_ratio * n), 1), n)
+            tau = float(np.sort(S)[n - k])
+            lo = (tau * (1 - SCORE_RTOL) - 2 * SCORE_ATOL) / (1 + SCORE_RTOL)
+            hi = (tau * (1 + SCORE_RTOL) + 2 * SCORE_ATOL) / (1 - SCORE_RTOL)
+            band_pop += int(np.count_nonzero((S >= lo) & (S <= hi)))
+            lh = l * H + h
+            kept = np.zeros(n, bool)
+            kept[idx[offsets[lh]:offsets[lh + 1]]] = True
+            sel_ok = sel_ok and bool(kept[S > hi].all()) and not bool(kept[S < lo].any()) \
+                and int(kept.sum()) == k
+    return {"max_rel_err": max_rel, "scores_within_tol": ok,
+            "near_tie_band": band_pop if mode == 0 else None,
+            "topk_outside_band_ok": sel_ok if mode == 0 else None,
+            "heads_checked": len(ref)}
 
 
 def main():
@@ -406,6 +450,21 @@ def main():
         else:
             kvq.kv_compact(dev["k_ctx"], dev["v_ctx"], offsets, idx, k_out, v_out, stream)
     cold_ms = cold_time_ms(torch, compact_only)
+    # the library's own streaming copy over the same byte count (half read,
+    # half written), also with nothing cached: the compaction's HBM reference
+    cbytes = work["merge_bytes" if args.merge else "compact_bytes"]
+    n16 = int(cbytes // 2) // 16
+    csrc = torch.empty(n16 * 16, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    copy_cold_ms = cold_time_ms(torch, lambda: kvq.kv_copy(csrc, cdst, stream))
+    stream_copy_gbs = 2.0 * n16 * 16 / (copy_cold_ms * 1e-3) / 1e9
+    del csrc, cdst
+
+    ref = cpu.pop("_ref_scores", None) if cpu else None
+    if args.device_inputs:   # the oracle ran on the generator's inputs, not these
+        ref = None
+    acc = accuracy_fields(ref, scores.cpu().numpy(), offsets.cpu().numpy(), idx.cpu().numpy(),
+                          w.keep_ratio, args.mode)
 
     ms_per_step = 1e3 * elapsed / args.steps
     value = w.context_pairs / (elapsed / args.steps)
@@ -456,14 +515,20 @@ def main():
         "lse_mfma_frac": round(lse_tf / PEAK_BF16_TFLOPS, 4),
         "colmax_mfma_frac": round(col_tf / PEAK_BF16_TFLOPS, 4),
         "compact_hbm_frac": round(cmp_gbs / PEAK_HBM_GBS, 4),
-        "compact_cold_hbm_frac": round(work["merge_bytes" if args.merge else "compact_bytes"]
-                                       / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "compact_cold_hbm_frac": round(cbytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        # the library's streaming copy of the same bytes, cold, and the cold
+        # compaction's rate as a fraction of it
+        "stream_copy_cold_gbs": round(stream_copy_gbs, 1),
+        "compact_cold_frac_of_copy": round(cbytes / (cold_ms * 1e-3) / 1e9 / stream_copy_gbs, 4),
         "select_gbs": round(sel_gbs, 1),
         "copy_gbs": round(copy_gbs, 1),
         # attainable dense bf16 rate (vendor GEMM, 8192^3) and the two
         # scoring passes' combined rate as a fraction of it
         "gemm_tflops": round(gemm_tflops, 1),
         "scoring_frac_of_gemm": round(scoring_tf / gemm_tflops, 4),
+        # GPU scores of the CPU baseline's heads against the oracle's
+        # (KVzip page, section 4.1: the band the budget decision guards)
+        **acc,
     }
     print(json.dumps(line), flush=True)
 

@@ -18,8 +18,9 @@
  *   section 4.1  - keep the r% highest-scoring pairs.
  *
  * Readings fixed by this library where the page is silent:
- *   - logits are scale * <q, k> with `scale` supplied by the caller
- *     (normally float32(1 / sqrt(d)));
+ *   - logits are scale * <q, k> with the model's attention temperature
+ *     scale = 1 / sqrt(d); the scoring calls take it as an argument, and
+ *     scale = 0 selects that default, float32(1 / sqrt(d)), formed here;
  *   - row i (0-based) of the pass sees all n_c cached keys and new keys
  *     0..i, its own included; every one of the n_in rows counts;
  *   - the softmax is normalised over every key a row sees, then sliced;
@@ -88,7 +89,10 @@ int kv_keep_count(int64_t n, double keep_ratio, int64_t* k_out);
  *   lse[l][h][g][i] = ln sum_{j seen by row i} exp(scale * <q_{g,i}, k_j>)
  * over the n_c cached keys and new keys 0..i.  The attention matrix is never
  * stored.  Requires L, H >= 1, 1 <= G <= 8, d in {64, 128, 256}, n_c >= 1,
- * n_prompt >= 0, G * (n_prompt + n_c) < 2^31, scale > 0 and finite. */
+ * n_prompt >= 0, G * (n_prompt + n_c) < 2^31, and scale = 0 (the default
+ * float32(1 / sqrt(d))) or a positive scale for which both 1 / scale and
+ * 1e30 * scale * log2(e) are finite in fp32 (about 3e-39 <= scale <= 2.3e8;
+ * the passes form both).  KV_ERR_INVALID_ARG otherwise. */
 int kvscore_lse(const void* q, const void* k_ctx, const void* k_new, float* lse,
                 int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
                 float scale, void* stream);
@@ -192,7 +196,9 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
 /* Compaction (KVzip section 2.1, KV_p as a subset of KV_c): for every head
  * (l, h) and every t in [offsets[l*H+h], offsets[l*H+h+1]) copies
  *   k_out[t] = k_ctx[l][h][idx[t]],  v_out[t] = v_ctx[l][h][idx[t]]
- * bit for bit.  total = offsets[L*H] (known on the host from kv_topk_total).
+ * bit for bit.  total = offsets[L*H] (known on the host from kv_topk_total),
+ * or any larger count of rows that idx, k_out and v_out hold: rows from
+ * offsets[L*H] on are then neither read nor written.
  * offsets must be non-decreasing with offsets[0] = 0; a row whose index falls
  * outside [0, n_c) is written as zeros instead of being read.  d in
  * {64, 128, 256}; L*H < 2^31, n_c < 2^31, 0 <= total <= L*H*n_c.  With
@@ -200,6 +206,13 @@ int kv_head_scores(const float* scores, int L, int H, int64_t n_c,
 int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
                const int32_t* idx, void* k_out, void* v_out, int L, int H,
                int d, int64_t n_c, int64_t total, void* stream);
+
+/* Plain device-to-device copy of `bytes` (a multiple of 16; src and dst
+ * 16-byte aligned, not overlapping), with the compaction's 16-byte
+ * non-temporal loads and eight loads in flight per thread.  Not a step of the
+ * method: the streaming reference that the compaction's HBM rate is read
+ * against. */
+int kv_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Gated merge instead of drop (page "Selective KV cache merging", section
  * 1: the soft cosine gate).  For kept row t (head lh with offsets[lh] <= t <

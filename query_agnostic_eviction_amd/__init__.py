@@ -7,7 +7,7 @@ compaction, as hand-written gfx950 HIP kernels in libkvq.so behind a C ABI
 fails loudly when the library has not been built.
 """
 from .api import (KvqError, epikv_evict, evict, kv_chunk_layout, kv_compact,
-                  kv_compact_tokens, kv_epi_deltas, kv_epi_scores, kv_keep_count,
+                  kv_compact_tokens, kv_copy, kv_epi_deltas, kv_epi_scores, kv_keep_count,
                   kv_head_scores, kv_merge_compact, kv_select_tokens,
                   kv_select_tokens_workspace_bytes, kv_status_string, kv_topk_select,
                   kv_topk_select_noalloc, kv_topk_total,

@@ -19,7 +19,7 @@ EXPORTS = (
     "kv_status_string", "kv_last_hip_error", "kv_keep_count", "kvscore_lse",
     "kvscore_colmax", "kv_chunk_layout", "kvscore_chunked_lse",
     "kvscore_chunked_colmax", "kv_topk_total", "kv_topk_workspace_bytes",
-    "kv_topk_select", "kv_topk_select_noalloc", "kv_head_scores", "kv_compact", "kv_epi_deltas",
+    "kv_topk_select", "kv_topk_select_noalloc", "kv_head_scores", "kv_compact", "kv_copy", "kv_epi_deltas",
     "kv_epi_scores", "kv_select_tokens_workspace_bytes", "kv_select_tokens",
     "kv_compact_tokens", "kv_merge_compact",
 )
@@ -70,6 +70,7 @@ def load() -> ctypes.CDLL:
         "kv_topk_select_noalloc": (i32, [vp, i32, i32, i64, f64, i32, vp, vp, i64, vp]),
         "kv_head_scores": (i32, [vp, i32, i32, i64, vp, vp]),
         "kv_compact": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, vp]),
+        "kv_copy": (i32, [vp, vp, i64, vp]),
         "kv_epi_deltas": (i32, [vp, i32, i64, i32, vp, vp]),
         "kv_epi_scores": (i32, [vp, i32, i32, i64, i32, f64, i32, vp, vp]),
         "kv_select_tokens_workspace_bytes": (sz, [i64]),

@@ -11,7 +11,6 @@ Compression with Context Reconstruction", sections 2.1 and 3.2):
 from __future__ import annotations
 
 import ctypes
-import math
 from typing import Optional, Tuple
 
 import torch
@@ -113,7 +112,7 @@ def kvscore_lse(q: torch.Tensor, k_ctx: torch.Tensor, k_new: torch.Tensor,
     _dev(lse, torch.float32, "lse")
     _size(lse, L * H * G * (n_c + n_prompt), "lse")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, float32(1 / sqrt(d))
     _check("kvscore_lse", _lib.load().kvscore_lse(
         _ptr(q), _ptr(k_ctx), _ptr(k_new), _ptr(lse), L, H, G, d, n_c, n_prompt,
         float(scale), _stream(stream)))
@@ -135,7 +134,7 @@ def kvscore_colmax(q: torch.Tensor, k_ctx: torch.Tensor, lse: torch.Tensor,
     _dev(scores, torch.float32, "scores")
     _size(scores, L * H * n_c, "scores")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, float32(1 / sqrt(d))
     _check("kvscore_colmax", _lib.load().kvscore_colmax(
         _ptr(q), _ptr(k_ctx), _ptr(lse), _ptr(scores), L, H, G, d, n_c, n_prompt,
         float(scale), _stream(stream)))
@@ -172,7 +171,7 @@ def kvscore_chunked_lse(q, k_ctx, k_new, G: int, n_prompt: int, chunk: int,
     if tuple(lse.shape) != (L, H, rows * G):
         raise ValueError("lse must be [L,H,rows*G]")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, float32(1 / sqrt(d))
     _check("kvscore_chunked_lse", _lib.load().kvscore_chunked_lse(
         _ptr(q), _ptr(k_ctx), _ptr(k_new), _ptr(lse), L, H, G, d, n_c, n_prompt,
         chunk, float(scale), _stream(stream)))
@@ -194,7 +193,7 @@ def kvscore_chunked_colmax(q, k_ctx, lse, G: int, n_prompt: int, chunk: int,
     _dev(scores, torch.float32, "scores")
     _size(scores, L * H * n_c, "scores")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, float32(1 / sqrt(d))
     _check("kvscore_chunked_colmax", _lib.load().kvscore_chunked_colmax(
         _ptr(q), _ptr(k_ctx), _ptr(lse), _ptr(scores), L, H, G, d, n_c, n_prompt,
         chunk, float(scale), _stream(stream)))
@@ -285,6 +284,8 @@ def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
     L, H, n_c, d = k_ctx.shape
     if offsets.numel() != L * H + 1:
         raise ValueError("offsets must hold L*H+1 entries")
+    # the rows idx and the outputs hold: the kept count offsets[L*H] (on the
+    # device) or more; the library writes only the kept rows
     total = idx.numel()
     if k_out is None:
         k_out = torch.empty((total, d), dtype=torch.bfloat16, device=k_ctx.device)
@@ -298,6 +299,19 @@ def kv_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,
         _ptr(k_ctx), _ptr(v_ctx), _ptr(offsets), _ptr(idx), _ptr(k_out), _ptr(v_out),
         L, H, d, n_c, total, _stream(stream)))
     return k_out, v_out
+
+
+def kv_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Plain streaming copy of src's bytes into dst (the HBM reference the
+    compaction is read against)."""
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check("kv_copy", _lib.load().kv_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+    return dst
 
 
 def kv_merge_compact(k_ctx: torch.Tensor, v_ctx: torch.Tensor, offsets: torch.Tensor,

@@ -67,7 +67,7 @@ KERNEL_SOURCES = {
     "kv_topk_select": "kv_topk.hip", "kv_topk_select_noalloc": "kv_topk.hip",
     "kv_head_scores": "kv_topk.hip",
     "kv_select_tokens": "kv_topk.hip", "kv_compact": "kv_compact.hip",
-    "kv_compact_tokens": "kv_compact.hip", "kv_epi_deltas": "epikv.hip",
+    "kv_compact_tokens": "kv_compact.hip", "kv_copy": "kv_compact.hip", "kv_epi_deltas": "epikv.hip",
     "kv_epi_scores": "epikv.hip", "kv_merge_compact": "selkv_merge.hip",
 }
 

@@ -11,7 +11,9 @@
 // row's source (head by binary search of the CSR offsets, then its index)
 // into an LDS table, so the copy itself is branch-free.  Every address is
 // bounded by (l*H+h) < L*H and 0 <= idx < n_c, so a malformed index yields a
-// zero row, never a stray read.
+// zero row, never a stray read.  `total` may exceed the kept count
+// offsets[L*H] (idx and the outputs sized with spare capacity): rows from
+// offsets[L*H] on are neither read nor written.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -39,10 +41,12 @@ __global__ __launch_bounds__(256) void compact_kernel(
   __shared__ int64_t src_row[kCpRows];  // lh * n_c + idx, or -1 for a zero row
 
   const int64_t t0 = (int64_t)blockIdx.x * kCpRows;
+  // rows this call writes: the kept rows, within the caller's total
+  const int64_t rows = SHARED ? total : min(total, offsets[LH]);
   if (threadIdx.x < kCpRows) {
     const int64_t t = t0 + threadIdx.x;
     int64_t r = -1;
-    if (t < total) {
+    if (t < rows) {
       int64_t lo, j;
       if (SHARED) {
         lo = t / shared_k;
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int64_t t = t0 + it * RPI + rr;
-    if (t < total) {
+    if (t < rows) {
       *reinterpret_cast<u32x4*>(k_out + (size_t)t * D + c * 8) = kv[it];
       *reinterpret_cast<u32x4*>(v_out + (size_t)t * D + c * 8) = vv[it];
     }
@@ -104,7 +108,45 @@ hipError_t launch_compact_d(const uint16_t* k_ctx, const uint16_t* v_ctx,
   return hipGetLastError();
 }
 
+// Plain device copy of n16 16-byte chunks: the streaming counterpart of the
+// gather above (same 16-byte non-temporal loads), with kCopyInFlight loads in
+// flight per thread before their stores, over a grid of a few waves of
+// workgroups per CU.
+constexpr int kCopyInFlight = 8;
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * kCopyInFlight;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kCopyInFlight + threadIdx.x; base < n16;
+       base += stride) {
+    u32x4 v[kCopyInFlight];
+#pragma unroll
+    for (int u = 0; u < kCopyInFlight; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      v[u] = i < n16 ? ldg16_once(src + i) : zero16();
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyInFlight; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t want = (n16 + 256 * kCopyInFlight - 1) / (256 * kCopyInFlight);
+  const int64_t grid = want < (int64_t)cus * 8 ? want : (int64_t)cus * 8;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
                           const int64_t* offsets, const int32_t* idx,

@@ -30,12 +30,25 @@ int64_t keep_count_of(int64_t n, double r) {
   return k;
 }
 
+// The logit scale of the scoring passes: 0 selects the model's temperature
+// float32(1 / sqrt(d)); otherwise it must be positive with 1 / scale and the
+// first running-max offset of pass 1, 1e30 * scale * log2(e), finite in fp32
+// (both are formed by the passes).  Returns 0 for a rejected scale.
+float resolve_scale(float scale, int d) {
+  if (scale == 0.0f) return (float)(1.0 / sqrt((double)d));
+  if (!(scale > 0.0f) || !isfinite(scale)) return 0.0f;
+  const float c2 = scale * kvq::kLog2e;
+  if (!isfinite(1.0e30f * c2) || !isfinite((float)(1.0 / (double)scale))) return 0.0f;
+  return scale;
+}
+
 // Shared checks of the two scoring passes.
 int check_score_args(int L, int H, int G, int d, int64_t n_c, int64_t n_prompt,
                      float scale, kvq::ScoreShape* out) {
   if (L < 1 || H < 1 || n_c < 1 || n_prompt < 0) return KV_ERR_INVALID_ARG;
-  if (!(scale > 0.0f) || !isfinite(scale)) return KV_ERR_INVALID_ARG;
   if (d != 64 && d != 128 && d != 256) return KV_ERR_UNSUPPORTED;
+  scale = resolve_scale(scale, d);
+  if (scale == 0.0f) return KV_ERR_INVALID_ARG;
   if (G < 1 || G > 8) return KV_ERR_UNSUPPORTED;
   const int64_t n_in = n_prompt + n_c;
   if (n_c >= (int64_t)1 << 31 || (int64_t)G * n_in >= (int64_t)1 << 31)
@@ -310,6 +323,14 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
       static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx),
       offsets, idx, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
       L * H, d, n_c, total, 0, static_cast<hipStream_t>(stream)));
+}
+
+int kv_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes < 0 || bytes % 16 != 0) return KV_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return KV_ERR_ALIGNMENT;
+  if (bytes == 0) return KV_OK;
+  (void)hipGetLastError();
+  return hip_status(kvq::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
 }
 
 int kv_epi_deltas(const void* h, int n_layers, int64_t n, int D, float* g, void* stream) {

@@ -15,7 +15,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs each
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // D += A * B on the 32x32x16 bf16 matrix core op.  Lane l supplies

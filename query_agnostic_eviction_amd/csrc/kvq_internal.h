@@ -6,6 +6,9 @@
 
 namespace kvq {
 
+// log2(e): the scoring passes take exp as exp2 with the logit scale folded in
+constexpr float kLog2e = 1.4426950408889634f;
+
 // Where one tensor of work item ("head") u lives, as an element offset:
 //   off0 + (u / inner) * outer + (u % inner) * step
 // An unchunked call has one work item per (layer, KV head) and inner = 1;
@@ -84,6 +87,9 @@ hipError_t launch_compact(const uint16_t* k_ctx, const uint16_t* v_ctx,
                           uint16_t* k_out, uint16_t* v_out, int LH, int d,
                           int64_t n_c, int64_t total, int64_t shared_k,
                           hipStream_t stream);
+
+// Plain streaming copy of `bytes` (a multiple of 16); see kv_copy.
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 // Top-k of n signed finite floats (ties to the lower index), ascending, by
 // the grid-wide select (workspace of global_select_workspace(n) bytes).

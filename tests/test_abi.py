@@ -109,8 +109,14 @@ def test_score_validation(lib, fn):
     assert fn(lib, H=-1) == INV
     assert fn(lib, n_c=0) == INV
     assert fn(lib, n_p=-1) == INV
-    for s in (0.0, -0.5, math.nan, math.inf):
+    for s in (-0.5, -0.0 - 1e-30, math.nan, math.inf, 2.4e8, 2e-39):
         assert fn(lib, scale=s) == INV
+    # accepted scales pass on to the pointer checks (a misaligned pointer
+    # then reports KV_ERR_ALIGNMENT without touching a device): 0 selects
+    # float32(1 / sqrt(d)); the range ends where 1e30 * scale * log2(e) or
+    # 1 / scale stops being finite in fp32
+    for s in (0.0, 0.1, 2.3e8, 3e-39):
+        assert fn(lib, scale=s, q=P2) == ALN
     for d in (0, 32, 96, 512):
         assert fn(lib, d=d) == UNS
     for g in (0, 9, -1):

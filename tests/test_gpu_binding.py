@@ -72,3 +72,53 @@ def test_empty_kept_sets():
     ko, vo = kvq.kv_compact_tokens(kc, vc, keep)
     torch.cuda.synchronize()
     assert torch.equal(ko, kc[:, :, keep.long()]) and torch.equal(vo, vc[:, :, keep.long()])
+
+
+def test_compact_with_spare_capacity():
+    """idx and the outputs may hold more rows than the kept set: the kept rows
+    are gathered bit for bit and the rows past offsets[L*H] stay untouched
+    (KVzip page, section 2.1: KV_p is a subset of KV_c)."""
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    print("compaction with spare capacity", flush=True)
+    dev = "cuda"
+    L, H, n_c, d, keep = 2, 3, 300, 128, 0.2
+    g = torch.Generator(device=dev).manual_seed(5)
+    kc = torch.randn((L, H, n_c, d), device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn((L, H, n_c, d), device=dev, generator=g).to(torch.bfloat16)
+    scores = torch.rand((L, H, n_c), device=dev, generator=g)
+    total = kvq.kv_topk_total(L, H, n_c, keep, 1)
+    spare = 37
+    offsets = torch.empty(L * H + 1, dtype=torch.int64, device=dev)
+    idx = torch.full((total + spare,), 12345, dtype=torch.int32, device=dev)  # garbage past the set
+    kvq.kv_topk_select(scores, keep, 1, offsets, idx[:total])
+    sentinel = torch.full((total + spare, d), -3.0, dtype=torch.bfloat16, device=dev)
+    ko, vo = sentinel.clone(), sentinel.clone()
+    kvq.kv_compact(kc, vc, offsets, idx, ko, vo)
+    torch.cuda.synchronize()
+    off = offsets.cpu().tolist()
+    assert off[-1] == total
+    ix = idx.cpu()
+    for lh in range(L * H):
+        l, h = divmod(lh, H)
+        rows = ix[off[lh]:off[lh + 1]].long()
+        assert torch.equal(ko[off[lh]:off[lh + 1]], kc[l, h][rows.to(dev)])
+        assert torch.equal(vo[off[lh]:off[lh + 1]], vc[l, h][rows.to(dev)])
+    assert torch.equal(ko[total:], sentinel[total:]) and torch.equal(vo[total:], sentinel[total:])
+
+
+def test_default_scale_is_float32_inverse_sqrt_d():
+    """scale omitted (0 at the C ABI) equals passing float32(1 / sqrt(d))."""
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    print("default scale", flush=True)
+    import numpy as np
+    dev = "cuda"
+    for d in (64, 128, 256):
+        L, H, G, n_c, n_p = 1, 2, 2, 200, 5
+        g = torch.Generator(device=dev).manual_seed(d)
+        q = torch.randn((L, H, G, n_c + n_p, d), device=dev, generator=g).to(torch.bfloat16)
+        kc = torch.randn((L, H, n_c, d), device=dev, generator=g).to(torch.bfloat16)
+        kn = torch.randn((L, H, n_c + n_p, d), device=dev, generator=g).to(torch.bfloat16)
+        s_def, l_def = kvq.score(q, kc, kn)
+        s_exp, l_exp = kvq.score(q, kc, kn, scale=float(np.float32(1.0 / np.sqrt(d))))
+        torch.cuda.synchronize()
+        assert torch.equal(s_def, s_exp) and torch.equal(l_def, l_exp)
