@@ -209,9 +209,9 @@ int kv_compact(const void* k_ctx, const void* v_ctx, const int64_t* offsets,
 
 /* Plain device-to-device copy of `bytes` (a multiple of 16; src and dst
  * 16-byte aligned, not overlapping), with the compaction's 16-byte
- * non-temporal loads and eight loads in flight per thread.  Not a step of the
- * method: the streaming reference that the compaction's HBM rate is read
- * against. */
+ * non-temporal loads and stores and four loads in flight per thread.  Not a
+ * step of the method: the streaming reference that the compaction's HBM rate
+ * is read against. */
 int kv_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Gated merge instead of drop (page "Selective KV cache merging", section

@@ -44,6 +44,11 @@ __device__ __forceinline__ u32x4 ldg16_once(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// 16-byte store of data this kernel does not read again: non-temporal
+__device__ __forceinline__ void stg16_once(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;
