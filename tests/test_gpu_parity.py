@@ -488,28 +488,34 @@ def _model_budget_checks(w, dev, sc, heads, S_ref):
                          f"head score ({l},{h})")
 
 
-GOLDEN_128K = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
-                           "llama3.1-8b-128k_head31-7.npz")
+def _golden_128k(l, h):
+    """The float64 oracle's stored values of one whole head of the 128K
+    workload (written by tests/golden/make_llama128k_head.py)."""
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        f"llama3.1-8b-128k_head{l}-{h}.npz")
 
 
 def test_llama8b_128k_full_size_sampled():
     w = synth.LLAMA8B_128K
     l, h = 0, 0
-    gl, gh_ = w.L - 1, w.H - 1      # the head stored by tests/golden/make_llama128k_head.py
+    gl, gh_ = w.L - 1, w.H - 1
     _say("case: full", w.name)
     dev, gens = _full_size_inputs(w, [(l, h), (gl, gh_)])
     out = _run(w, dev)
-    # whole-head parity against the float64 oracle's stored values
-    gold = np.load(GOLDEN_128K)
-    assert (int(gold["layer"]), int(gold["head"])) == (gl, gh_)
-    S_gold = gold["scores"].astype(np.float64)
-    check_scores(out["scores"][gl, gh_].cpu().numpy(), S_gold, f"scores[{gl},{gh_}]")
-    check_lse(out["lse"][gl, gh_].cpu().numpy()[:, ::16], gold["lse_rows16"].astype(np.float64),
-              f"lse[{gl},{gh_}] every 16th row")
+    # whole-head parity of the first and the last head against the float64
+    # oracle's stored values: every score, the lse of every 16th row, and the
+    # kept set outside the near-tie band
     k = oracle.keep_count(w.n_c, w.keep_ratio)
-    band = check_topk_band(head_kept(out["offsets"].cpu().numpy(), out["idx"].cpu().numpy(),
-                                     gl * w.H + gh_), S_gold, k)
-    _say(f"head ({gl},{gh_}): whole head within tolerance, near-tie band holds {band} keys")
+    for (hl, hh) in ((l, h), (gl, gh_)):
+        gold = np.load(_golden_128k(hl, hh))
+        assert (int(gold["layer"]), int(gold["head"])) == (hl, hh)
+        S_gold = gold["scores"].astype(np.float64)
+        check_scores(out["scores"][hl, hh].cpu().numpy(), S_gold, f"scores[{hl},{hh}]")
+        check_lse(out["lse"][hl, hh].cpu().numpy()[:, ::16],
+                  gold["lse_rows16"].astype(np.float64), f"lse[{hl},{hh}] every 16th row")
+        band = check_topk_band(head_kept(out["offsets"].cpu().numpy(), out["idx"].cpu().numpy(),
+                                         hl * w.H + hh), S_gold, k)
+        _say(f"head ({hl},{hh}): whole head within tolerance, near-tie band holds {band} keys")
     gh = gens[(l, h)]
     q, kc, kn = oracle.workload_head_inputs(gh)
     lse_g = out["lse"][l, h].cpu().numpy()

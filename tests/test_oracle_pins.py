@@ -480,3 +480,4 @@ def test_select_signed_zero_equals_zero():
     assert oracle.epikv.select_tokens(s.reshape(-1), 4).tolist() == [0, 1, 2, 4]
     s2 = np.abs(s)
     assert np.array_equal(oracle.select(s2, 4 / 6 + 1e-9, 0)[1], idx)
+
