@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace kvq {
 

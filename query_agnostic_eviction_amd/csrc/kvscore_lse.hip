@@ -34,8 +34,10 @@
 //    per-logit max.  Logits of keys a row must not see are set to -inf after
 //    the products of the few subtiles that hold such keys (under a uniform
 //    branch; the paired schedule seeds its accumulators instead).
-//  * Subtile sums enter each lane's running sum with Kahan compensation
-//    (per subtile, not per logit), so 128K-key rows stay at fp32 accuracy.
+//  * Sums enter each lane's running sum with Kahan compensation, so 128K-key
+//    rows stay at fp32 accuracy: once per tile with the staggered schedule
+//    (a tile's four subtile sums are first added plainly), once per subtile
+//    with the paired one.
 //  * With the staggered schedule a wave stops computing after the last tile
 //    holding a key its rows see (and a wave holding no rows computes
 //    nothing); it keeps issuing its share of the tile loads and joining the
@@ -47,6 +49,16 @@ namespace kvq {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int D>
 struct LseCfg {
@@ -194,12 +206,57 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // thousands of subtile sums of similar size, whose rounding errors would
   // otherwise accumulate
   float sum[NFQ], comp[NFQ];
+  // staggered schedule: a tile's subtile sums are added plainly into tp and
+  // enter the compensated sum once per tile
+  float tp[NFQ];
 #pragma unroll
   for (int f = 0; f < NFQ; ++f) {
     m[f] = kNegBig;
-    sum[f] = comp[f] = 0.f;
+    sum[f] = comp[f] = tp[f] = 0.f;
   }
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
+
+  auto kahan_add = [&](float v, int f) __attribute__((always_inline)) {
+    const float y = v - comp[f];
+    const float t = sum[f] + y;
+    comp[f] = (t - sum[f]) - y;
+    sum[f] = t;
+  };
+  // fold one fragment's 16 logits per lane (a subtile) into its tile sum and,
+  // with FOLD, the tile sum into the running sum
+  auto reduce_t = [&](const f32x16& x, auto f_tag, auto fold_tag) __attribute__((always_inline)) {
+    constexpr int f = decltype(f_tag)::value;
+    constexpr bool FOLD = decltype(fold_tag)::value;
+    float nmc = -m[f] * c2;
+    float e[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) e[a] = fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+#pragma unroll
+    for (int a = 4; a < 16; ++a) e[a & 3] += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+    float ts = (e[0] + e[1]) + (e[2] + e[3]);
+    if (!(ts <= kRescaleAt)) {
+      float tm = x[0];
+#pragma unroll
+      for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
+      const float mn = __builtin_fmaxf(m[f], tm);
+      const float rescale = fast_exp2((m[f] - mn) * c2);
+      sum[f] *= rescale;
+      comp[f] *= rescale;
+      tp[f] *= rescale;
+      m[f] = mn;
+      nmc = -mn * c2;
+      float t = 0.f;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
+      ts = t;
+    }
+    if constexpr (FOLD) {
+      kahan_add(tp[f] + ts, f);
+      tp[f] = 0.f;
+    } else {
+      tp[f] += ts;
+    }
+  };
 
   // fold one fragment's 16 logits per lane (a subtile) into its running sum
   auto reduce = [&](const f32x16& x, auto f_tag) __attribute__((always_inline)) {
@@ -285,8 +342,9 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   for (int a = 0; a < 16; ++a) pend[a] = -__builtin_inff();
 
   // one 32-key subtile
-  auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase)
+  auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase, auto sub_tag)
                      __attribute__((always_inline)) {
+    constexpr int SUB = decltype(sub_tag)::value;
     if constexpr (C::STAGGER) {
       bf16x8 ak[C::KS];
 #pragma unroll
@@ -296,7 +354,11 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
         f32x16 c = {};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) c = mfma32(ak[s], qop(f_tag, s), c);
-        reduce(pend, std::integral_constant<int, (f + NFQ - 1) % NFQ>{});
+        // the pending fragment belongs to the previous subtile for f = 0:
+        // it closes a tile when that subtile was the tile's last
+        constexpr bool FOLD = f == 0 ? SUB == 0 : SUB == C::NSUB - 1;
+        reduce_t(pend, std::integral_constant<int, (f + NFQ - 1) % NFQ>{},
+                 std::integral_constant<bool, FOLD>{});
         if (masked) mask(c, f, seg, kbase);
         pend = c;
         // keep the next fragment's work from being hoisted into this one
@@ -336,15 +398,17 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     const bool masked = seg == 0 ? (key0 + C::KT > n_c)
                                  : (key0 + C::KT - 1 > pos_min || key0 + C::KT > n_in);
     const uint16_t* sb = sk + BUF * TL::ELEMS;
+    auto all_subtiles = [&](bool msk) __attribute__((always_inline)) {
+      static_for<C::NSUB>([&](auto sub_tag) __attribute__((always_inline)) {
+        constexpr int sub = decltype(sub_tag)::value;
+        subtile(sb + sub * 32 * D, msk, seg, key0 + sub * 32, sub_tag);
+      });
+    };
     if (C::STAGGER || !masked) {
       // (staggered: one copy, the mask applied under a uniform branch)
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, C::STAGGER && masked, seg, key0 + sub * 32);
+      all_subtiles(C::STAGGER && masked);
     } else {
-#pragma unroll
-      for (int sub = 0; sub < C::NSUB; ++sub)
-        subtile(sb + sub * 32 * D, true, seg, key0 + sub * 32);
+      all_subtiles(true);
     }
     wait_all_mem();
     __syncthreads();
@@ -368,7 +432,11 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     wait_all_mem();
     __syncthreads();
   }
-  if constexpr (C::STAGGER) reduce(pend, std::integral_constant<int, NFQ - 1>{});
+  if constexpr (C::STAGGER) {
+    reduce_t(pend, std::integral_constant<int, NFQ - 1>{}, std::true_type{});
+#pragma unroll
+    for (int f = 0; f < NFQ; ++f) kahan_add(tp[f], f);   // (0 after whole tiles)
+  }
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll

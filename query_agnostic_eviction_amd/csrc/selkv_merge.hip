@@ -196,8 +196,9 @@ __global__ __launch_bounds__(256) void merge_kernel(
     ks[e] = ks[e] / w;
     vs[e] = vs[e] / w;
   }
-  *reinterpret_cast<u32x4*>(k_out + t * D + sub * 8) = narrow8(ks);
-  *reinterpret_cast<u32x4*>(v_out + t * D + sub * 8) = narrow8(vs);
+  // written once and not read again here: non-temporal stores
+  stg16_once(k_out + t * D + sub * 8, narrow8(ks));
+  stg16_once(v_out + t * D + sub * 8, narrow8(vs));
   if (mass != nullptr && sub == 0) mass[t] = msum;
 }
 

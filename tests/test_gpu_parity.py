@@ -127,6 +127,32 @@ def test_ragged_shapes(case):
         _select_checks(w, gen, out, S_ref, [(l, h) for l in range(L) for h in range(H)], mode)
 
 
+def _tile_boundary_cases():
+    """G = 1 shapes whose row count G * n_in and key count sit on either side
+    of one and two 32 KB tiles (16384 / d rows or keys): pass 2's last row
+    tile is shifted back to end at the last row (rows seen twice), or clamped
+    when all rows fit in one tile; pass 1's key tiles end ragged or exact."""
+    out = []
+    for d in (64, 128, 256):
+        qt = 16384 // d
+        for rows in (qt - 1, qt, qt + 1, 2 * qt - 1, 2 * qt + 1):
+            out.append((d, rows - 3, 3))       # n_in = rows, n_c = rows - 3
+    return out
+
+
+@pytest.mark.parametrize("case", _tile_boundary_cases(),
+                         ids=[f"d{c[0]}-nc{c[1]}" for c in _tile_boundary_cases()])
+def test_tile_boundaries(case):
+    d, n_c, n_p = case
+    w = synth.LLAMA8B_8K.shrink(G=1, d=d, n_c=n_c, n_prompt=n_p, L=1, H=2,
+                                rank=min(synth.LLAMA8B_8K.rank, d))
+    _say("case: tile boundary", case)
+    gen = synth.generate_workload(w, workers=1)
+    out = _run(w, _upload(gen), 0)
+    S_ref = _full_check(w, gen, out)
+    _select_checks(w, gen, out, S_ref, [(0, 0), (0, 1)], 0)
+
+
 EXTREME = [
     # (G, d, n_c, n_prompt, H)
     (2, 64, 300, 5, 2),
