@@ -50,13 +50,17 @@ def algorithmic_work(w, mode=0, chunk=None):
         logits1 += G * (n_in * m + n_in * (n_in + 1) // 2)   # every seen key, every row
         logits2 += G * n_in * m                              # cached columns only
     total = synth_total(w, mode)
+    # HBM reads of the scores per select: a segment of at most 32,768 scores
+    # (mode 0: a head, mode 1: a layer) is staged in LDS once; longer ones are
+    # read by 3 histogram passes and 1 ordered pass; mode 2 reads 5 times
+    seg = n_c if mode == 0 else w.H * n_c
+    reads = 5 if mode == 2 else (1 if seg <= 32768 else 4)
     return {
         "lse_flops": 2.0 * d * logits1 * heads,
         "lse_exps": float(logits1 * heads),
         "colmax_flops": 2.0 * d * logits2 * heads,
-        # scores read by 3 histogram passes and 1 ordered pass (mode 2 adds a
-        # counting pass); idx + offsets written
-        "select_bytes": 4.0 * (5 if mode == 2 else 4) * heads * n_c + 4.0 * total
+        # scores read, idx + offsets written
+        "select_bytes": 4.0 * reads * heads * n_c + 4.0 * total
                         + 8.0 * (heads + 1),
         # K and V rows read and written, plus the index of each row
         "compact_bytes": 2.0 * 2 * 2 * d * total + 4.0 * total,

@@ -13,7 +13,10 @@
 //  2. one ordered pass keeps every score above T and the lowest-index scores
 //     equal to T, writing kept positions in ascending order through two
 //     block-wide prefix sums per chunk.
-// The result is unique (ties go to the lower index) and bit-exact.
+// A segment of up to 32,768 scores (a head of up to 32K cached pairs) is
+// first staged in LDS (128 KB), so the four passes read global memory once;
+// longer segments are read by each pass.  The result is unique (ties go to
+// the lower index) and bit-exact.
 #include <mutex>
 
 #include "kvq_device.h"
@@ -72,19 +75,48 @@ __device__ __forceinline__ uint32_t sort_key(uint32_t v) {
   return (v & 0x80000000u) ? ~v : (v | 0x80000000u);
 }
 
-template <bool SIGNED>
+// Segments of at most kTkStage scores are staged in LDS once and every pass
+// reads them there; longer ones are read from global memory by each pass.
+// One 1024-thread block with the full stage fits a compute unit's LDS.
+constexpr int kTkStage = 32768;  // 128 KB
+
+template <bool SIGNED, bool STAGED>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(
     const uint32_t* __restrict__ scores, int H, int n_c, int mode, int seg_len,
     int k, int nseg, int64_t* __restrict__ offsets, int32_t* __restrict__ idx) {
   __shared__ int hist[2048];
   __shared__ int sm[2 * kTkWaves];
   __shared__ int sel[2];
+  __shared__ uint32_t stage[STAGED ? kTkStage : 1];
 
   const int tid = threadIdx.x;
   const int seg = blockIdx.x;
   const uint32_t* data = scores + (size_t)seg * seg_len;
   const int64_t out_base = (int64_t)seg * k;
   const unsigned useg = (unsigned)seg_len;  // < 2^31: unsigned index math cannot wrap
+  if constexpr (STAGED) {
+    // kHistBatch loads in flight per thread, then the LDS writes
+    for (unsigned base = 0; base < useg; base += kTkThreads * kHistBatch) {
+      uint32_t v[kHistBatch];
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const unsigned j = base + u * kTkThreads + tid;
+        v[u] = j < useg ? data[j] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const unsigned j = base + u * kTkThreads + tid;
+        if (j < useg) stage[j] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  // the bits of score j (j < useg); the sort key is applied by the caller,
+  // after the value arrives, so a batch of global loads stays in flight
+  auto raw_at = [&](unsigned j) -> uint32_t {
+    if constexpr (STAGED) return stage[j];
+    else return data[j];
+  };
 
   // ---- 1. radix select of the k-th largest bit pattern -------------------
   uint32_t prefix = 0, pmask = 0;
@@ -103,7 +135,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
 #pragma unroll
       for (int u = 0; u < kHistBatch; ++u) {
         const unsigned j = base + u * kTkThreads + tid;
-        v[u] = j < useg ? data[j] : 0u;
+        v[u] = j < useg ? raw_at(j) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kHistBatch; ++u) {
@@ -152,7 +184,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
 #pragma unroll
     for (int i = 0; i < kTkItems; ++i) {
       const unsigned j = j0 + i;
-      v[i] = j < useg ? sort_key<SIGNED>(data[j]) : 0u;
+      v[i] = j < useg ? sort_key<SIGNED>(raw_at(j)) : 0u;
       neq += (j < useg && v[i] == T) ? 1 : 0;
     }
     int eq_tot;
@@ -563,9 +595,14 @@ hipError_t launch_topk(const float* scores, int L, int H, int n_c, int mode,
                        hipStream_t stream) {
   const int nseg = mode == 0 ? L * H : L;
   const int seg_len = mode == 0 ? n_c : H * n_c;
-  hipLaunchKernelGGL(topk_kernel<false>, dim3(nseg), dim3(kTkThreads), 0, stream,
-                     reinterpret_cast<const uint32_t*>(scores), H, n_c, mode,
-                     seg_len, (int)k_per_segment, nseg, offsets, idx);
+  if (seg_len <= kTkStage)
+    hipLaunchKernelGGL((topk_kernel<false, true>), dim3(nseg), dim3(kTkThreads), 0, stream,
+                       reinterpret_cast<const uint32_t*>(scores), H, n_c, mode,
+                       seg_len, (int)k_per_segment, nseg, offsets, idx);
+  else
+    hipLaunchKernelGGL((topk_kernel<false, false>), dim3(nseg), dim3(kTkThreads), 0, stream,
+                       reinterpret_cast<const uint32_t*>(scores), H, n_c, mode,
+                       seg_len, (int)k_per_segment, nseg, offsets, idx);
   return hipGetLastError();
 }
 

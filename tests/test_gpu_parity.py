@@ -207,7 +207,10 @@ def test_keep_all_is_identity():
         assert np.array_equal(dev_bf16_bits(out["v_out"]), gen["v_ctx"].reshape(-1, w.d))
 
 
-@pytest.mark.parametrize("n_c,L,H", [(5000, 2, 3), (20000, 1, 2), (8193, 2, 1), (1, 3, 2), (7, 1, 4)])
+# the last four sit at the LDS-staging limit of 32,768 scores per segment:
+# mode 0 segments of 32,768 and 32,769, mode 1 segments (H * n_c) likewise
+@pytest.mark.parametrize("n_c,L,H", [(5000, 2, 3), (20000, 1, 2), (8193, 2, 1), (1, 3, 2), (7, 1, 4),
+                                     (32768, 1, 2), (32769, 1, 1), (8192, 2, 4), (10923, 1, 3)])
 def test_select_ties_bit_exact(n_c, L, H):
     rng = np.random.default_rng(n_c + L + H)
     # few distinct values: long runs of exact ties across chunk boundaries
