@@ -81,7 +81,6 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   using TL = Tile<D>;
   constexpr int NFQ = C::NFQ;
   const int G = sh.G, n_c = sh.n_c, n_in = sh.n_in;
-  const float scale = sh.scale;
   __shared__ __attribute__((aligned(1024))) uint16_t sk[2 * TL::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -91,11 +90,14 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // latest positions (most keys) first
   const int wgi = wg_per_head - 1 - logical % wg_per_head;
 
-  // workgroup bookkeeping: its first position and how far its new keys go
+  // workgroup bookkeeping: its first position and how far its new keys go.
+  // (Integer division runs on the vector unit; readfirstlane returns these
+  // uniform values to scalar registers, so the per-tile tests that use them
+  // stay scalar.)
   const int F_first = C::FPW * wgi;
   const int F_last = min(C::FPW * wgi + C::FPW - 1, nfrag_head - 1);
-  const int pos_min = 32 * (F_first / G);
-  const int new_len = min(n_in, 32 * (F_last / G + 1));
+  const int pos_min = __builtin_amdgcn_readfirstlane(32 * (F_first / G));
+  const int new_len = __builtin_amdgcn_readfirstlane(min(n_in, 32 * (F_last / G + 1)));
 
   // the wave's fragments (uniform per wave)
   int fg[NFQ], fpos0[NFQ];
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   for (int f = 0; f < NFQ; ++f) {
     const int F = C::FPW * wgi + NFQ * wave + f;
     fvalid[f] = F < nfrag_head;
-    fg[f] = fvalid[f] ? F % G : 0;
-    fpos0[f] = fvalid[f] ? 32 * (F / G) : 0;
+    fg[f] = __builtin_amdgcn_readfirstlane(fvalid[f] ? F % G : 0);
+    fpos0[f] = __builtin_amdgcn_readfirstlane(fvalid[f] ? 32 * (F / G) : 0);
     if (fvalid[f]) wave_last = max(wave_last, min(fpos0[f] + 31, n_in - 1));
   }
 
@@ -201,7 +203,10 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // stay far from overflow (< 2^64 per subtile) and terms far below m only
   // underflow where they are negligible, so the result is exact to fp32
   // rounding while the hot path costs one FMA, one exp2 and one add per logit.
-  float m[NFQ];
+  // m is kept as nm = -m * c2, the exp2 argument's offset, so the hot path
+  // does not form it (rounding is monotone, so raising m is a min on nm and
+  // gives the same nm as forming it from the raised m).
+  float nm[NFQ];
   // running sums with a compensation term (Kahan): long contexts add
   // thousands of subtile sums of similar size, whose rounding errors would
   // otherwise accumulate
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   float tp[NFQ];
 #pragma unroll
   for (int f = 0; f < NFQ; ++f) {
-    m[f] = kNegBig;
+    nm[f] = -kNegBig * c2;
     sum[f] = comp[f] = tp[f] = 0.f;
   }
   constexpr float kRescaleAt = 18446744073709551616.0f;  // 2^64
@@ -227,24 +232,28 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   auto reduce_t = [&](const f32x16& x, auto f_tag, auto fold_tag) __attribute__((always_inline)) {
     constexpr int f = decltype(f_tag)::value;
     constexpr bool FOLD = decltype(fold_tag)::value;
-    float nmc = -m[f] * c2;
+    float nmc = nm[f];
     float e[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) e[a] = fast_exp2(__builtin_fmaf(x[a], c2, nmc));
 #pragma unroll
     for (int a = 4; a < 16; ++a) e[a & 3] += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
     float ts = (e[0] + e[1]) + (e[2] + e[3]);
-    if (!(ts <= kRescaleAt)) {
+    // the whole wave takes the rare path when one lane needs it (for the
+    // others it keeps or raises their max and re-sums: the same result up to
+    // rounding); a wave-uniform branch keeps the tile loop free of
+    // execution-mask handling
+    if (__builtin_amdgcn_ballot_w64(!(ts <= kRescaleAt))) {
       float tm = x[0];
 #pragma unroll
       for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
-      const float mn = __builtin_fmaxf(m[f], tm);
-      const float rescale = fast_exp2((m[f] - mn) * c2);
+      const float nmn = __builtin_fminf(nm[f], -tm * c2);
+      const float rescale = fast_exp2(nmn - nm[f]);
       sum[f] *= rescale;
       comp[f] *= rescale;
       tp[f] *= rescale;
-      m[f] = mn;
-      nmc = -mn * c2;
+      nm[f] = nmn;
+      nmc = nmn;
       float t = 0.f;
 #pragma unroll
       for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // fold one fragment's 16 logits per lane (a subtile) into its running sum
   auto reduce = [&](const f32x16& x, auto f_tag) __attribute__((always_inline)) {
     constexpr int f = decltype(f_tag)::value;
-    float nmc = -m[f] * c2;
+    float nmc = nm[f];
     // four running partial sums keep few temporaries live
     float e[4];
 #pragma unroll
@@ -274,12 +283,12 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
       float tm = x[0];
 #pragma unroll
       for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
-      const float mn = __builtin_fmaxf(m[f], tm);
-      const float rescale = fast_exp2((m[f] - mn) * c2);
+      const float nmn = __builtin_fminf(nm[f], -tm * c2);
+      const float rescale = fast_exp2(nmn - nm[f]);
       sum[f] *= rescale;
       comp[f] *= rescale;
-      m[f] = mn;
-      nmc = -mn * c2;
+      nm[f] = nmn;
+      nmc = nmn;
       float t = 0.f;
 #pragma unroll
       for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   // both fragments of the paired schedule at once: their exps interleave and
   // one test covers the rare path of either
   auto reduce_pair = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
-    const float nmc[2] = {-m[0] * c2, -m[1] * c2};
+    const float nmc[2] = {nm[0], nm[1]};
     float e[2][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -442,11 +451,12 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
 #pragma unroll
   for (int f = 0; f < NFQ; ++f) {
     const float own = sum[f] - comp[f];
-    const float mo = __shfl_xor(m[f], 32);
+    const float nmo = __shfl_xor(nm[f], 32);
     const float so = __shfl_xor(own, 32);
-    const float M = __builtin_fmaxf(m[f], mo);
-    const float S = own * fast_exp2((m[f] - M) * c2) + so * fast_exp2((mo - M) * c2);
-    const float val = __builtin_fmaf(M, scale, __logf(S));
+    const float nM = __builtin_fminf(nm[f], nmo);  // -(row max) * c2
+    const float S = own * fast_exp2(nM - nm[f]) + so * fast_exp2(nM - nmo);
+    // row max * scale = -nM * ln 2 (c2 = scale * log2 e)
+    const float val = __builtin_fmaf(-nM, kLn2, __logf(S));
     const int pos = fpos0[f] + (lane & 31);
     if (lane < 32 && fvalid[f] && pos < n_in)
       lse[map_offset(sh.lse, u, sh.inner) + (size_t)fg[f] * n_in + pos] = val;
