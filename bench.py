@@ -482,7 +482,7 @@ def main():
     sel_gbs = work["select_bytes"] / (ms["kv_topk_select"] * 1e-3) / 1e9
 
     dominant = max(names, key=lambda n: ms[n])
-    traffic = recorded_traffic(dominant, w.name) if not chunk else None
+    traffic = recorded_traffic(dominant, w.name + (f"-chunk{chunk}" if chunk else ""))
     if dominant in ("kvscore_lse", "kvscore_colmax"):
         achieved = lse_tf if dominant == "kvscore_lse" else col_tf
         roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
