@@ -18,30 +18,25 @@
 //    A operand and the queries as B, so each lane holds 16 keys of one query:
 //    the softmax sums stay lane-local; the two half-waves that share a query
 //    merge once at the end.
-//  * d <= 128 (four fragments per wave): a 32-key subtile's key operands are
-//    read from LDS once into registers and feed the products of all four
-//    fragments, which are staggered: while the matrix core runs the chain of
-//    fragment f, the VALU reduces the logits of fragment f - 1 (for f = 0,
-//    the last fragment of the previous subtile).  Only two sets of
-//    accumulators are live, which is what leaves room for four fragments'
-//    queries (128 registers at d = 128).
-//  * d = 256 (two fragments per wave): a subtile's key operands would take
-//    64 registers, so each is read once and fed to both fragments at once;
-//    the subtile is reduced right after its own products and the other wave
-//    on the SIMD provides the overlap.
+//  * A 32-key subtile's key operands are read from LDS once into registers
+//    and feed the products of all the wave's fragments (four at d <= 128,
+//    two at d = 256, where a fragment's queries take twice the registers),
+//    which are staggered: while the matrix core runs the chain of fragment
+//    f, the VALU reduces the logits of fragment f - 1 (for f = 0, the last
+//    fragment of the previous subtile).  Only two sets of accumulators are
+//    live, which is what leaves room for the fragments' queries (128
+//    registers).
 //  * exp is taken as exp2 with the scale folded into one FMA per logit; the
-//    running max is updated lazily (see reduce), so the hot path has no
+//    running max is updated lazily (see reduce_t), so the hot path has no
 //    per-logit max.  Logits of keys a row must not see are set to -inf after
 //    the products of the few subtiles that hold such keys (under a uniform
-//    branch; the paired schedule seeds its accumulators instead).
-//  * Sums enter each lane's running sum with Kahan compensation, so 128K-key
-//    rows stay at fp32 accuracy: once per tile with the staggered schedule
-//    (a tile's four subtile sums are first added plainly), once per subtile
-//    with the paired one.
-//  * With the staggered schedule a wave stops computing after the last tile
-//    holding a key its rows see (and a wave holding no rows computes
-//    nothing); it keeps issuing its share of the tile loads and joining the
-//    barriers.
+//    branch).
+//  * Sums enter each lane's running sum with Kahan compensation once per
+//    tile (a tile's subtile sums are first added plainly), so 128K-key rows
+//    stay at fp32 accuracy.
+//  * A wave stops computing after the last tile holding a key its rows see
+//    (and a wave holding no rows computes nothing); it keeps issuing its
+//    share of the tile loads and joining the barriers.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -68,8 +63,6 @@ struct LseCfg {
   // query fragments per wave: each key operand read feeds NFQ matrix ops
   static constexpr int NFQ = D == 256 ? 2 : 4;
   static constexpr int FPW = 4 * NFQ;      // fragments per workgroup
-  // staggered fragments (key operands of a subtile held in registers)
-  static constexpr bool STAGGER = D != 256;
 };
 
 template <int D>
@@ -142,34 +135,19 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   const int T0 = (n_c + C::KT - 1) / C::KT;
   const int T1 = (new_len + C::KT - 1) / C::KT;
   const int T = T0 + T1;
-  // tiles this wave computes on: with the staggered schedule every
-  // cached-key tile and the new-key tiles up to its last position; the
-  // paired schedule sweeps the workgroup's tiles
-  const int Tw = !C::STAGGER ? T : (wave_last < 0 ? 0 : T0 + (wave_last + C::KT) / C::KT);
+  // tiles this wave computes on: every cached-key tile and the new-key
+  // tiles up to its last position
+  const int Tw = wave_last < 0 ? 0 : T0 + (wave_last + C::KT) / C::KT;
 
-  // Per-thread parts of the tile-load and key-operand addresses.  The
-  // staggered schedule has no registers to spare: two values each, combined
-  // on the fly.  The paired schedule reads a key operand per product pair,
-  // so there a table per load slot and per k-step keeps that arithmetic off
-  // the reads.
+  // Per-thread parts of the tile-load and key-operand addresses (no
+  // registers to spare: two values each, combined on the fly)
   const int rel01[2] = {TL::src_rel(0, tid), TL::src_rel(1, tid)};
   const int rd_base = TL::read_base(lane), rd_x = TL::read_x(lane);
-  int rel_t[C::STAGGER ? 1 : TL::LOADS], rd_t[C::STAGGER ? 1 : C::KS];
-  if constexpr (!C::STAGGER) {
-#pragma unroll
-    for (int i = 0; i < TL::LOADS; ++i) rel_t[i] = TL::src_rel(i, tid);
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) rd_t[s] = TL::read_off(lane, s);
-  }
   auto load_rel = [&](int i) __attribute__((always_inline)) {
-    if constexpr (C::STAGGER) return TL::src_rel_from(rel01, i);
-    else return rel_t[i];
+    return TL::src_rel_from(rel01, i);
   };
   auto key_op = [&](const uint16_t* sb, int s) __attribute__((always_inline)) -> bf16x8 {
-    if constexpr (C::STAGGER)
-      return *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
-    else
-      return *reinterpret_cast<const bf16x8*>(sb + rd_t[s]);
+    return *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
   };
 
   // LDS-DMA of tile t into buffer `buf`; rows past the segment end re-read
@@ -267,71 +245,6 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     }
   };
 
-  // fold one fragment's 16 logits per lane (a subtile) into its running sum
-  auto reduce = [&](const f32x16& x, auto f_tag) __attribute__((always_inline)) {
-    constexpr int f = decltype(f_tag)::value;
-    float nmc = nm[f];
-    // four running partial sums keep few temporaries live
-    float e[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) e[a] = fast_exp2(__builtin_fmaf(x[a], c2, nmc));
-#pragma unroll
-    for (int a = 4; a < 16; ++a) e[a & 3] += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
-    float ts = (e[0] + e[1]) + (e[2] + e[3]);
-    if (!(ts <= kRescaleAt)) {
-      // rare path: raise the running max to this subtile's max and re-sum
-      float tm = x[0];
-#pragma unroll
-      for (int a = 1; a < 16; ++a) tm = __builtin_fmaxf(tm, x[a]);
-      const float nmn = __builtin_fminf(nm[f], -tm * c2);
-      const float rescale = fast_exp2(nmn - nm[f]);
-      sum[f] *= rescale;
-      comp[f] *= rescale;
-      nm[f] = nmn;
-      nmc = nmn;
-      float t = 0.f;
-#pragma unroll
-      for (int a = 0; a < 16; ++a) t += fast_exp2(__builtin_fmaf(x[a], c2, nmc));
-      ts = t;
-    }
-    const float y = ts - comp[f];
-    const float t = sum[f] + y;
-    comp[f] = (t - sum[f]) - y;
-    sum[f] = t;
-  };
-
-  // both fragments of the paired schedule at once: their exps interleave and
-  // one test covers the rare path of either
-  auto reduce_pair = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
-    const float nmc[2] = {nm[0], nm[1]};
-    float e[2][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) e[f][a] = fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
-#pragma unroll
-    for (int a = 4; a < 16; ++a)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) e[f][a & 3] += fast_exp2(__builtin_fmaf(x[f][a], c2, nmc[f]));
-    float ts[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) ts[f] = (e[f][0] + e[f][1]) + (e[f][2] + e[f][3]);
-    if (!(ts[0] <= kRescaleAt) || !(ts[1] <= kRescaleAt)) {
-      // rare path: redo with the per-fragment reduction, which raises the
-      // running max of whichever fragment needs it
-      reduce(x[0], std::integral_constant<int, 0>{});
-      reduce(x[1], std::integral_constant<int, 1>{});
-      return;
-    }
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const float y = ts[f] - comp[f];
-      const float t = sum[f] + y;
-      comp[f] = (t - sum[f]) - y;
-      sum[f] = t;
-    }
-  };
-
   // Masking: logits of keys a row must not see (cached-key tail past n_c, new
   // keys past the row's position or past n_in) become -inf, which the
   // reduction turns into 0.
@@ -354,47 +267,28 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
   auto subtile = [&](const uint16_t* sb, bool masked, int seg, int kbase, auto sub_tag)
                      __attribute__((always_inline)) {
     constexpr int SUB = decltype(sub_tag)::value;
-    if constexpr (C::STAGGER) {
-      bf16x8 ak[C::KS];
+    bf16x8 ak[C::KS];
 #pragma unroll
-      for (int s = 0; s < C::KS; ++s) ak[s] = key_op(sb, s);
-      auto frag = [&](auto f_tag) __attribute__((always_inline)) {
-        constexpr int f = decltype(f_tag)::value;
-        f32x16 c = {};
+    for (int s = 0; s < C::KS; ++s) ak[s] = key_op(sb, s);
+    auto frag = [&](auto f_tag) __attribute__((always_inline)) {
+      constexpr int f = decltype(f_tag)::value;
+      f32x16 c = {};
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) c = mfma32(ak[s], qop(f_tag, s), c);
-        // the pending fragment belongs to the previous subtile for f = 0:
-        // it closes a tile when that subtile was the tile's last
-        constexpr bool FOLD = f == 0 ? SUB == 0 : SUB == C::NSUB - 1;
-        reduce_t(pend, std::integral_constant<int, (f + NFQ - 1) % NFQ>{},
-                 std::integral_constant<bool, FOLD>{});
-        if (masked) mask(c, f, seg, kbase);
-        pend = c;
-        // keep the next fragment's work from being hoisted into this one
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      frag(std::integral_constant<int, 0>{});
-      if constexpr (NFQ > 1) frag(std::integral_constant<int, 1>{});
-      if constexpr (NFQ > 2) frag(std::integral_constant<int, 2>{});
-      if constexpr (NFQ > 3) frag(std::integral_constant<int, 3>{});
-    } else {
-      static_assert(NFQ == 2, "paired schedule holds two fragments");
-      // masked subtiles start from a -inf seed where a row must not see a key
-      f32x16 c[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const f32x16 z = {};
-        c[f] = z;
-        if (masked) mask(c[f], f, seg, kbase);
-      }
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const bf16x8 a = key_op(sb, s);
-        c[0] = mfma32(a, qop(std::integral_constant<int, 0>{}, s), c[0]);
-        c[1] = mfma32(a, qop(std::integral_constant<int, 1>{}, s), c[1]);
-      }
-      reduce_pair(c);
-    }
+      for (int s = 0; s < C::KS; ++s) c = mfma32(ak[s], qop(f_tag, s), c);
+      // the pending fragment belongs to the previous subtile for f = 0: it
+      // closes a tile when that subtile was the tile's last
+      constexpr bool FOLD = f == 0 ? SUB == 0 : SUB == C::NSUB - 1;
+      reduce_t(pend, std::integral_constant<int, (f + NFQ - 1) % NFQ>{},
+               std::integral_constant<bool, FOLD>{});
+      if (masked) mask(c, f, seg, kbase);
+      pend = c;
+      // keep the next fragment's work from being hoisted into this one
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    frag(std::integral_constant<int, 0>{});
+    if constexpr (NFQ > 1) frag(std::integral_constant<int, 1>{});
+    if constexpr (NFQ > 2) frag(std::integral_constant<int, 2>{});
+    if constexpr (NFQ > 3) frag(std::integral_constant<int, 3>{});
   };
 
   // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
@@ -407,18 +301,11 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     const bool masked = seg == 0 ? (key0 + C::KT > n_c)
                                  : (key0 + C::KT - 1 > pos_min || key0 + C::KT > n_in);
     const uint16_t* sb = sk + BUF * TL::ELEMS;
-    auto all_subtiles = [&](bool msk) __attribute__((always_inline)) {
-      static_for<C::NSUB>([&](auto sub_tag) __attribute__((always_inline)) {
-        constexpr int sub = decltype(sub_tag)::value;
-        subtile(sb + sub * 32 * D, msk, seg, key0 + sub * 32, sub_tag);
-      });
-    };
-    if (C::STAGGER || !masked) {
-      // (staggered: one copy, the mask applied under a uniform branch)
-      all_subtiles(C::STAGGER && masked);
-    } else {
-      all_subtiles(true);
-    }
+    // one copy of the tile loop: the mask is applied under a uniform branch
+    static_for<C::NSUB>([&](auto sub_tag) __attribute__((always_inline)) {
+      constexpr int sub = decltype(sub_tag)::value;
+      subtile(sb + sub * 32 * D, masked, seg, key0 + sub * 32, sub_tag);
+    });
     wait_all_mem();
     __syncthreads();
   };
@@ -441,11 +328,9 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(
     wait_all_mem();
     __syncthreads();
   }
-  if constexpr (C::STAGGER) {
-    reduce_t(pend, std::integral_constant<int, NFQ - 1>{}, std::true_type{});
+  reduce_t(pend, std::integral_constant<int, NFQ - 1>{}, std::true_type{});
 #pragma unroll
-    for (int f = 0; f < NFQ; ++f) kahan_add(tp[f], f);   // (0 after whole tiles)
-  }
+  for (int f = 0; f < NFQ; ++f) kahan_add(tp[f], f);   // (0 after whole tiles)
 
   // merge the two half-waves that hold the same query, then store
 #pragma unroll
