@@ -50,3 +50,29 @@ def test_algorithmic_work_counts_the_defined_logits(G, d, n_c, n_prompt, chunk):
     k = oracle.keep_count(n_c, w.keep_ratio)
     assert work["kept_rows"] == heads * k
     assert work["compact_bytes"] == heads * k * (2 * 2 * 2 * d + 4)
+
+
+def _stage_limit():
+    """The per-segment LDS staging limit of the top-k kernel, read from its
+    source so that bench.py's byte count follows the kernel."""
+    import re
+    src = open(os.path.join(ROOT, "query_agnostic_eviction_amd", "csrc", "kv_topk.hip")).read()
+    return int(re.search(r"constexpr int kTkStage = (\d+);", src).group(1))
+
+
+@pytest.mark.parametrize("mode,H,n_c", [(0, 3, 8192), (0, 2, 40000), (1, 8, 4096), (1, 8, 4097),
+                                        (2, 4, 100)])
+def test_select_bytes_follow_the_staging_limit(mode, H, n_c):
+    # a segment (a head in mode 0, a layer's H * n_c scores in mode 1) that
+    # fits the LDS stage is read once; longer ones four times; the grid-wide
+    # model budget (mode 2) five times
+    lim = _stage_limit()
+    w = synth.TINY.shrink(L=2, H=H, n_c=n_c)
+    seg = n_c if mode == 0 else H * n_c
+    reads = 5 if mode == 2 else (1 if seg <= lim else 4)
+    heads = w.L * H
+    total = bench.synth_total(w, mode)
+    work = bench.algorithmic_work(w, mode)
+    assert work["select_bytes"] == 4.0 * reads * heads * n_c + 4.0 * total + 8.0 * (heads + 1)
+    if mode == 1:
+        assert (seg <= lim) == (n_c == 4096)   # the two cases straddle the limit
