@@ -703,3 +703,22 @@ def test_one_million_key_head():
     # the model-wide budget over the same 2^20 scores equals mode 0 here
     o2, i2 = kvq.kv_topk_select(out["scores"], w.keep_ratio, 2)
     assert torch.equal(i2, out["idx"]) and torch.equal(o2, out["offsets"])
+
+
+# the compaction's head search over many heads, empty heads among them
+@pytest.mark.parametrize("L,H", [(1, 1), (16, 128), (1, 2049), (3, 1000)])
+def test_compact_many_heads(L, H):
+    _say("case: compact heads", L, H)
+    rng = np.random.default_rng(L * H)
+    n_c, d = 9, 64
+    k = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
+    v = rng.integers(0, 2 ** 16, size=(L, H, n_c, d), dtype=np.uint16)
+    counts = rng.integers(0, n_c + 1, size=L * H)       # empty heads included
+    counts[0] = n_c
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    idx = np.concatenate([np.sort(rng.choice(n_c, size=c, replace=False)) for c in counts]).astype(np.int32)
+    ko, vo = kvq.kv_compact(to_dev_bf16(k), to_dev_bf16(v), torch.from_numpy(off).cuda(),
+                            torch.from_numpy(idx).cuda())
+    rko, rvo = oracle.compact(k, v, off, idx)
+    assert np.array_equal(dev_bf16_bits(ko), rko)
+    assert np.array_equal(dev_bf16_bits(vo), rvo)
