@@ -130,16 +130,11 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
     f32x16 c[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) c[f] = init;
-    // the subtile's query operands are read from LDS at once, so that the
-    // reads of later k-steps are in flight while the first ones are used
-    bf16x8 a[C::KS];
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      a[s] = *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
 #pragma unroll
-      for (int f = 0; f < NF; ++f) c[f] = mfma32(a[s], bk[f][s], c[f]);
+      for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], c[f]);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f)
