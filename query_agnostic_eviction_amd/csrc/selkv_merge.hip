@@ -37,11 +37,23 @@ __device__ __forceinline__ u32x4 narrow8(const float* x) {
   return u;
 }
 
-// Sum over the LPR lanes of a row group (aligned, power of two).
+// Sum over the LPR lanes of a row group (aligned, LPR in {8, 16, 32}).
+// Within a 16-lane row the butterfly runs on DPP lane permutations (no LDS
+// round trip): swap neighbours, swap pairs, mirror the 8-lane halves (which
+// adds the other quad's sum), mirror the row (which adds the other half's);
+// the two rows of a 32-lane group are then combined by a lane shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row groups of 8, 16 or 32 lanes");
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_f32<0x141>(x);  // row_half_mirror: lane 7 - i within each 8
+  if constexpr (LPR >= 16) x += dpp_f32<0x140>(x);  // row_mirror: 15 - i
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
   return x;
 }
 
