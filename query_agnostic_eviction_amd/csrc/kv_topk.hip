@@ -37,24 +37,36 @@ constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kTkItems = 8;  // consecutive scores per thread per chunk
 constexpr int kHistBatch = 16;  // loads in flight per thread in a histogram pass
 
+// The DPP value of lane i's partner under ctrl (0 where the partner is out
+// of range, or in rows row_mask leaves out).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave on DPP lane
+// permutations, with no LDS round trip: a shift-and-add ladder within each
+// 16-lane row (row_shr 1, 2, 4, 8), then the last lane of row 0 (and of
+// row 2) broadcast into the next row, and the last lane of row 1 into rows
+// 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i32<0x111>(v);        // row_shr:1
+  v += dpp_i32<0x112>(v);        // row_shr:2
+  v += dpp_i32<0x114>(v);        // row_shr:4
+  v += dpp_i32<0x118>(v);        // row_shr:8
+  v += dpp_i32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_i32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Exclusive prefix sum of x over the block; *total gets the block sum.
 __device__ __forceinline__ int block_excl_scan(int x, int* sm, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  const int v = wave_incl_scan(x);
   if (lane == 63) sm[wave] = v;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kTkWaves ? sm[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < kTkWaves; o <<= 1) {
-      const int y = __shfl_up(w, o);
-      if (lane >= o) w += y;
-    }
+    const int w = wave_incl_scan(lane < kTkWaves ? sm[lane] : 0);
     if (lane < kTkWaves) sm[kTkWaves + lane] = w;
   }
   __syncthreads();
@@ -208,7 +220,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(
       if (mode == 1 && j < useg && j % (unsigned)n_c == 0)
         offsets[(int64_t)seg * H + j / (unsigned)n_c] = out_base + pos;
       if (keep[i]) {
-        if (pos < k) idx[out_base + pos] = (int32_t)(mode == 1 ? j % (unsigned)n_c : j);
+        if ((unsigned)pos < (unsigned)k)
+          idx[out_base + pos] = (int32_t)(mode == 1 ? j % (unsigned)n_c : j);
         ++pos;
       }
     }
@@ -258,17 +271,29 @@ __device__ __forceinline__ bool last_to_arrive(GlobalState* st) {
   return last;
 }
 
+// One step of the 64-bit DPP ladder: v + (lane partner's v), the partner's
+// two halves moved by the same permutation (0 where out of range).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ unsigned long long dpp_add64(unsigned long long v) {
+  const unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+  const unsigned plo = (unsigned)dpp_i32<CTRL, ROW_MASK>((int)lo);
+  const unsigned phi = (unsigned)dpp_i32<CTRL, ROW_MASK>((int)hi);
+  return v + (((unsigned long long)phi << 32) | plo);
+}
+
 // Exclusive prefix sum over a 256-thread block (64-bit); *total = block sum.
 __device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long long x,
                                                                  unsigned long long* sm,
                                                                  unsigned long long* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the ladder of wave_incl_scan
   unsigned long long v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  v = dpp_add64<0x111>(v);
+  v = dpp_add64<0x112>(v);
+  v = dpp_add64<0x114>(v);
+  v = dpp_add64<0x118>(v);
+  v = dpp_add64<0x142, 0xA>(v);
+  v = dpp_add64<0x143, 0xC>(v);
   if (lane == 63) sm[wave] = v;
   __syncthreads();
   unsigned long long before = 0, tot = 0;
@@ -476,7 +501,7 @@ __global__ __launch_bounds__(kGThreads) void gsel_write(const uint32_t* __restri
       const long long j = j0 + i;
       if (offsets && j < b1 && j % n_c == 0) offsets[j / n_c] = (int64_t)pos;
       if (keep[i]) {
-        if ((long long)pos < k) idx[pos] = (int32_t)(j % n_c);
+        if (pos < (unsigned long long)k) idx[pos] = (int32_t)(j % n_c);
         ++pos;
       }
     }
