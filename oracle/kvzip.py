@@ -130,7 +130,7 @@ def row_lse(q_row: np.ndarray, i: int, k_ctx: np.ndarray, k_new: np.ndarray,
 
 
 # ----------------------------------------------------------------------------
-# parallel driver over row blocks of one head (threads, one BLAS thread each)
+# parallel runner over row blocks of one head (threads, one BLAS thread each)
 # ----------------------------------------------------------------------------
 def head_scores_parallel(q, k_ctx, k_new, scale, workers: int,
                          row_block: int = 128):

@@ -1,5 +1,5 @@
 """bench.py's per-run accuracy fields: the largest relative score error, the
-tolerance verdict and the near-tie band around each head's budget threshold
+within-tolerance flag and the near-tie band around each head's budget threshold
 (KVzip page, "KVzip: Query-Agnostic KV Cache Compression with Context
 Reconstruction", section 4.1), on hand-made scores whose answers are known."""
 import os

@@ -1,6 +1,6 @@
-"""bench.py's command-line contract: one JSON line with the fields the
-benchmark driver reads (GPU), and a clear refusal of more than one GPU (CPU:
-the refusal comes before anything touches a device)."""
+"""bench.py's command-line contract: one JSON line with the documented
+fields (GPU), and a clear refusal of more than one GPU (CPU: the refusal
+comes before anything touches a device)."""
 import json
 import os
 import subprocess
