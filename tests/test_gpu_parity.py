@@ -610,6 +610,11 @@ CHUNKED = [
     ("gemma3-12b-16k", 2, 256, 300, 5, 64, 1, 2),
     ("qwen2.5-14b-32k", 5, 128, 77, 0, 1, 1, 1),
     ("llama3.1-8b-8k", 3, 128, 70, 3, 1000, 1, 1),
+    # several chunks per workgroup in pass 1, in groups of up to four chunks
+    # of one head: 5 full chunks per head (groups of 4 and 1) over 2 x 2
+    # heads, and 6 per head (4 and 2) over 3 heads at d = 256
+    ("llama3.1-8b-8k", 4, 128, 700, 8, 128, 2, 2),
+    ("gemma3-12b-16k", 2, 256, 384, 4, 64, 1, 3),
 ]
 
 
