@@ -25,6 +25,11 @@
 //    which leaves a maximum unchanged.  Together with per-lane operand
 //    offsets formed on the fly this keeps four fragments per wave within
 //    the registers of two waves per SIMD.
+//  * Within a tile the query-operand reads from LDS run one k-step ahead of
+//    the products, and each subtile's seed is formed while the previous
+//    subtile's products run, so neither waits on LDS latency in front of the
+//    matrix ops (except at a tile's first subtile, whose data arrives with
+//    the tile).
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
@@ -117,9 +122,9 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
 #pragma unroll
   for (int f = 0; f < NF; ++f) M[f] = -__builtin_inff();
 
-  // one 32-row subtile: seed with -lse/scale of the lane's 16 rows, run the
-  // products, fold them into the running maxima
-  auto subtile = [&](const uint16_t* sb, const float* slb) {
+  // -lse/scale of the lane's 16 rows of a 32-row subtile: the seed of its
+  // products' accumulators
+  auto seed = [&](const float* slb) {
     f32x16 init;
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
@@ -127,31 +132,45 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) init[4 * grp + e] = -v[e] * inv_scale;
     }
-    f32x16 c[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) c[f] = init;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
-#pragma unroll
-      for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], c[f]);
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        M[f] = max3f(M[f], c[f][4 * g4], max3f(c[f][4 * g4 + 1], c[f][4 * g4 + 2], c[f][4 * g4 + 3]));
+    return init;
+  };
+  auto qread = [&](const uint16_t* sb, int s) {
+    return *reinterpret_cast<const bf16x8*>(sb + rd_base + 16 * (s ^ rd_x));
   };
 
   // tile t sits in buffer BUF: prefetch t+1 into the other buffer, consume
-  // t, then wait for the prefetch and publish it with one barrier
+  // t, then wait for the prefetch and publish it with one barrier.  Within
+  // the tile the operand reads run one k-step ahead of the products, and a
+  // subtile's seed is formed while the previous subtile's products run.
   auto step = [&](int t, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     if (t + 1 < T) issue_tile(t + 1, BUF ^ 1);
     const uint16_t* sb = sq + BUF * TL::ELEMS;
     const float* slb = sl + BUF * C::QT;
+    f32x16 init = seed(slb);
+    bf16x8 a = qread(sb, 0);
 #pragma unroll
-    for (int sub = 0; sub < C::NSUB; ++sub) subtile(sb + sub * 32 * D, slb + sub * 32);
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const uint16_t* sbs = sb + sub * 32 * D;
+      f32x16 c[NF];
+      f32x16 init_next;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        bf16x8 a_next;
+        if (s + 1 < C::KS) a_next = qread(sbs, s + 1);
+        else if (sub + 1 < C::NSUB) a_next = qread(sbs + 32 * D, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], s == 0 ? init : c[f]);
+        if (s == C::KS / 2 && sub + 1 < C::NSUB) init_next = seed(slb + (sub + 1) * 32);
+        a = a_next;
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          M[f] = max3f(M[f], c[f][4 * g4], max3f(c[f][4 * g4 + 1], c[f][4 * g4 + 2], c[f][4 * g4 + 3]));
+      if (sub + 1 < C::NSUB) init = init_next;
+    }
     wait_all_mem();
     __syncthreads();
   };
