@@ -52,7 +52,9 @@ struct ColCfg {
 
 // SMALL: fewer rows than one tile (G * n_in < QT); the tile then clamps rows
 // past the last one to the last row (duplicates again).
-template <int D, bool SMALL>
+// PIN: each k-step's operand read is pinned after its first product (see the
+// tile loop); the launcher sets it where a head's query stream is moderate.
+template <int D, bool SMALL, bool PIN>
 __global__ __launch_bounds__(256, 2) void colmax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_ctx,
     const float* __restrict__ lse, float* __restrict__ scores,
@@ -156,11 +158,22 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
       f32x16 init_next;
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {
+        // With PIN: the first product, then the next operand's read, then
+        // the other products.  The wait for an LDS read here drains every
+        // outstanding one, so a read issued right before the wait for the
+        // current operand is waited for at once; placed after the first
+        // product, it is covered by the other three, and the wait before the
+        // next k-step drains it alone.
+        if constexpr (PIN) {
+          c[0] = mfma32(a, bk[0][s], s == 0 ? init : c[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         bf16x8 a_next;
         if (s + 1 < C::KS) a_next = qread(sbs, s + 1);
         else if (sub + 1 < C::NSUB) a_next = qread(sbs + 32 * D, 0);
+        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], s == 0 ? init : c[f]);
+        for (int f = PIN ? 1 : 0; f < NF; ++f) c[f] = mfma32(a, bk[f][s], s == 0 ? init : c[f]);
         if (s == C::KS / 2 && sub + 1 < C::NSUB) init_next = seed(slb + (sub + 1) * 32);
         a = a_next;
       }
@@ -193,6 +206,14 @@ __global__ __launch_bounds__(256, 2) void colmax_kernel(
   }
 }
 
+// The pinned operand reads make a k-step's products wait less on LDS (about
+// 2 % faster, measured on MI355X at 8K, 32K and d = 256 16K contexts), but
+// with a long query stream per head (134 MB at a 128K context) the
+// workgroups of a head then drift apart over the sweep and read it from HBM
+// many times over (13x the traffic, 1.5 % slower).  Pinned up to this many
+// bytes of queries per work item; above, the compiler's order.
+constexpr long long kPinQueryBytes = 64ll << 20;
+
 template <int D>
 hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
                            const float* lse, float* scores, const ScoreShape& s,
@@ -205,12 +226,16 @@ hipError_t launch_colmax_d(const uint16_t* q, const uint16_t* k_ctx,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c2 = s.scale * kLog2e;
   const float inv_scale = (float)(1.0 / (double)s.scale);
-  if ((long long)s.G * s.n_in < ColCfg<D>::QT)
-    hipLaunchKernelGGL((colmax_kernel<D, true>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
+  const long long rows = (long long)s.G * s.n_in;
+  if (rows < ColCfg<D>::QT)
+    hipLaunchKernelGGL((colmax_kernel<D, true, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
+  else if (rows * D * 2 <= kPinQueryBytes)
+    hipLaunchKernelGGL((colmax_kernel<D, false, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
   else
-    hipLaunchKernelGGL((colmax_kernel<D, false>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
+    hipLaunchKernelGGL((colmax_kernel<D, false, false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, k_ctx, lse, scores, s, wg_per_head, c2, inv_scale);
   return hipGetLastError();
 }
 
