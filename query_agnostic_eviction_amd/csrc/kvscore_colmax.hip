@@ -27,9 +27,11 @@
 //    the registers of two waves per SIMD.
 //  * Within a tile the query-operand reads from LDS run one k-step ahead of
 //    the products, and each subtile's seed is formed while the previous
-//    subtile's products run, so neither waits on LDS latency in front of the
-//    matrix ops (except at a tile's first subtile, whose data arrives with
-//    the tile).
+//    subtile's products run (a tile's first subtile waits: its data arrives
+//    with the tile).  The compiler's waits on LDS reads drain every
+//    outstanding read, so where a work item's query stream is moderate each
+//    read is also pinned after its k-step's first product, which keeps it
+//    off the wait for the current operand (PIN below).
 //  * No atomics: each workgroup owns its columns, writes them once, and the
 //    result is independent of scheduling.
 #include "kvq_device.h"
